@@ -1,0 +1,110 @@
+"""TEST INFRASTRUCTURE -- the fp64 CPU oracle for exact attention.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``exact_self_attention_amd``) and neither imports the other.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+query rows); this module only compiles it with gcc, loads it with ctypes and
+marshals numpy arrays.  Inputs are float32 arrays holding the exact widening of
+the fp16/bf16 bit patterns the GPU reads; outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+             "-ffp-contract=off", "-fno-fast-math"]
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc into ``out`` (always recompiles)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str = _LIB, *, build_if_missing: bool = True) -> ctypes.CDLL:
+    lib = ctypes.CDLL(path) if os.path.exists(path) else None
+    if lib is None:
+        if not build_if_missing:
+            raise FileNotFoundError(path)
+        build(out=path)
+        lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_sdpa_rows.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double,
+                                     ctypes.c_int, p, p, i64, p, p]
+    lib.oracle_sdpa_rows.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def max_threads(lib: Optional[ctypes.CDLL] = None) -> int:
+    return (lib or _get()).oracle_max_threads()
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def sdpa_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
+    """Oracle attention on selected rows.
+
+    Q, K, V: float32 ``[B, H, N, d]``; ``key_len``: int ``[B]`` or None;
+    ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE ``[n]``)
+    in float64.
+    """
+    lib = lib or _get()
+    Q = np.ascontiguousarray(Q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    if Q.ndim != 4 or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must share one [B, H, N, d] shape")
+    B, H, N, d = Q.shape
+    sel = np.ascontiguousarray(sel, dtype=np.int64).reshape(-1, 3)
+    n = sel.shape[0]
+    O = np.zeros((n, d), dtype=np.float64)
+    LSE = np.zeros((n,), dtype=np.float64)
+    kl = None
+    if key_len is not None:
+        kl = np.ascontiguousarray(key_len, dtype=np.int32)
+        if kl.shape != (B,):
+            raise ValueError("key_len must have shape [B]")
+    rc = lib.oracle_sdpa_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d,
+                              float(scale), int(bool(causal)),
+                              None if kl is None else _ptr(kl),
+                              _ptr(sel), n, _ptr(O), _ptr(LSE))
+    if rc != 0:
+        raise ValueError("oracle_sdpa_rows rejected its arguments")
+    return O, LSE
+
+
+def sdpa(Q, K, V, scale, causal: bool = False, key_len=None, *, lib=None):
+    """Oracle attention on every row: O ``[B,H,N,d]`` and LSE ``[B,H,N]`` (float64)."""
+    Q = np.ascontiguousarray(Q, dtype=np.float32)
+    B, H, N, d = Q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    sel = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    O, LSE = sdpa_rows(Q, K, V, scale, causal, key_len, sel, lib=lib)
+    return O.reshape(B, H, N, d), LSE.reshape(B, H, N)

@@ -1,0 +1,137 @@
+/*
+ * TEST INFRASTRUCTURE -- not part of the product path.
+ *
+ * Plain, slow, fp64 CPU oracle for exact scaled-dot-product attention.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes, for every selected (batch b, head h, query row i):
+ *
+ *   S_ij = scale * (q_i . k_j)            for every visible key j
+ *   P_ij = exp(S_ij - max_j S_ij) / sum_j exp(S_ij - max_j S_ij)
+ *   O_i  = sum_j P_ij v_j
+ *   LSE_i = max_j S_ij + log(sum_j exp(S_ij - max_j S_ij))
+ *
+ * This is the textbook definition O = softmax(Q K^T / sqrt(d)) V of
+ * "Tensor Parallelism with CUDA - Standard Attention" (sections "Step 1:
+ * QK^T", "What is a Dot Product?", "Step 2: Softmax" -- the max-subtracted,
+ * numerically stable form -- and "Step 3: PV"), with the scale passed in as
+ * an argument, and the masked five-step form of "Naive Attention Kernel"
+ * (section 1, "Standard Attention: Step by Step") where the mask is
+ * structural: a masked key gets probability exactly zero.
+ *
+ * Visible keys (the readings this oracle fixes where the pages are silent):
+ *   - key j is visible iff j < L_b, where L_b = clamp(key_len[b], 0, N) when a
+ *     key-length array is given (a key-side padding mask, "cuda-reranker"),
+ *     else L_b = N;
+ *   - with causal masking additionally j <= i (top-left alignment, equal query
+ *     and key lengths);
+ *   - a row with no visible key has O_i = 0 and LSE_i = -inf.
+ *
+ * The score row is materialised in full (one row at a time), followed by two
+ * passes (max, then exponential sum), then the weighted sum of value rows.
+ * Inputs are float32 arrays holding the exact widening of the fp16/bf16 bits
+ * under test; all arithmetic is double precision with the C library's exp and
+ * log.  Built without fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Q, K, V: [B, H, N, d] row-major float32.
+ * key_len: [B] or NULL.
+ * sel: n_sel triples (b, h, i) as int64.
+ * O: [n_sel, d] double; LSE: [n_sel] double.
+ * Returns 0, or -1 on a bad argument or a failed allocation.
+ */
+int oracle_sdpa_rows(const float *Q, const float *K, const float *V,
+                     int64_t B, int64_t H, int64_t N, int64_t d,
+                     double scale, int causal, const int32_t *key_len,
+                     const int64_t *sel, int64_t n_sel,
+                     double *O, double *LSE)
+{
+    if (B < 0 || H < 0 || N < 0 || d <= 0 || n_sel < 0) return -1;
+    for (int64_t t = 0; t < n_sel; ++t) {
+        int64_t b = sel[3 * t], h = sel[3 * t + 1], i = sel[3 * t + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return -1;
+    }
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *p = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (s == NULL || p == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < n_sel; ++t) {
+            if (s == NULL || p == NULL) continue;
+            int64_t b = sel[3 * t], h = sel[3 * t + 1], i = sel[3 * t + 2];
+            const float *q  = Q + ((b * H + h) * N + i) * d;
+            const float *kb = K + (b * H + h) * N * d;
+            const float *vb = V + (b * H + h) * N * d;
+            double *o = O + t * d;
+
+            /* visible keys are j < n_vis */
+            int64_t L = N;
+            if (key_len != NULL) {
+                L = key_len[b];
+                if (L < 0) L = 0;
+                if (L > N) L = N;
+            }
+            int64_t n_vis = L;
+            if (causal && i + 1 < n_vis) n_vis = i + 1;
+
+            if (n_vis == 0) {
+                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                LSE[t] = -INFINITY;
+                continue;
+            }
+
+            /* scores S_ij = scale * q_i . k_j */
+            for (int64_t j = 0; j < n_vis; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += (double)q[c] * (double)kb[j * d + c];
+                s[j] = scale * dot;
+            }
+            /* pass 1: row maximum */
+            double m = s[0];
+            for (int64_t j = 1; j < n_vis; ++j)
+                if (s[j] > m) m = s[j];
+            /* pass 2: normaliser, then probabilities */
+            double l = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j) {
+                p[j] = exp(s[j] - m);
+                l += p[j];
+            }
+            for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;
+            /* O_i = sum_j P_ij v_j */
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j)
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += p[j] * (double)vb[j * d + c];
+            LSE[t] = m + log(l);
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -1 : 0;
+}

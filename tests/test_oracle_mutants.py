@@ -1,0 +1,60 @@
+"""Each plausible slip in the oracle must be caught by at least one pin.
+
+The oracle source is copied, one textual change is applied (a dropped term, a
+wrong sign, a wrong operand or index, an off-by-one in a mask), the copy is
+compiled with the oracle's own gcc flags into a temporary directory, and every
+pin in oracle_pin_checks.py is run against it.  A mutant that passes every pin
+means the pins leave that part of the oracle unchecked.  Only mutations that
+keep every memory access in bounds are used.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pin_checks as pins
+
+MUTANTS = {
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "exp_sign_flipped": ("p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
+    "exp2_for_exp": ("p[j] = exp(s[j] - m);", "p[j] = exp2(s[j] - m);"),
+    "no_normalisation": ("for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;", ""),
+    "causal_strict": ("if (causal && i + 1 < n_vis) n_vis = i + 1;",
+                      "if (causal && i < n_vis) n_vis = i;"),
+    "causal_ignored": ("if (causal && i + 1 < n_vis) n_vis = i + 1;", ""),
+    "key_len_ignored": ("L = key_len[b];", "L = N;"),
+    "key_operand_for_query": ("dot += (double)q[c] * (double)kb[j * d + c];",
+                              "dot += (double)kb[j * d + c] * (double)kb[j * d + c];"),
+    "key_operand_for_value": ("o[c] += p[j] * (double)vb[j * d + c];",
+                              "o[c] += p[j] * (double)kb[j * d + c];"),
+    "weight_dropped": ("o[c] += p[j] * (double)vb[j * d + c];",
+                       "o[c] += (double)vb[j * d + c];"),
+    "lse_without_max": ("LSE[t] = m + log(l);", "LSE[t] = log(l);"),
+    "lse_log2": ("LSE[t] = m + log(l);", "LSE[t] = m + log2(l);"),
+    "min_for_max": ("if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    "dot_offset": ("double dot = 0.0;", "double dot = 1.0;"),
+    "empty_row_lse_zero": ("LSE[t] = -INFINITY;", "LSE[t] = 0.0;"),
+    "value_row_skipped": ("for (int64_t j = 0; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +=",
+                          "for (int64_t j = 1; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +="),
+    "query_row_off_by_one": ("const float *q  = Q + ((b * H + h) * N + i) * d;",
+                             "const float *q  = Q + ((b * H + h) * N + (i > 0 ? i - 1 : 0)) * d;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle._SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = str(tmp_path / "liboracle_mutant.so")
+    oracle.build(src=str(mutated), out=so)
+    lib = oracle.load(so, build_if_missing=False)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"mutant {name} passes every pin"
