@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+A step is one attn_fwd launch over one batch of seeded synthetic inputs that
+are already resident in device memory.  The default workload is the causal
+decoder prefill B=1 H=32 N=4096 d=128 fp16 (scale 1/sqrt(128)), the
+configuration whose throughput is reported as TFLOP/s and as a fraction of
+the dense fp16 matrix-core peak.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-probe       # a plain device copy of known size, for
+                                     # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal ×½) + % of MI355X MFMA peak"
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "exact_self_attention_amd", "csrc", "fwd_fused.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU seconds of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true")
+    return ap.parse_args()
+
+
+def metric_flops(w) -> float:
+    """The metric's FLOP count: 4 B H N^2 d, halved when causal."""
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
+
+
+def visible_pairs(w, key_len=None) -> int:
+    """Visible (query, key) pairs: the algorithmic unit of work (4d flops each)."""
+    total = 0
+    for b in range(w.B):
+        L = w.N if key_len is None else int(min(max(key_len[b], 0), w.N))
+        if w.causal:
+            # sum over i of min(L, i + 1)
+            pairs = L * (L + 1) // 2 + (w.N - L) * L
+        else:
+            pairs = w.N * L
+        total += pairs * w.H
+    return total
+
+
+def algorithmic_bytes(w, key_len=None) -> int:
+    """Q and O once, K and V rows once per visible row, LSE once (4 B per row)."""
+    elem = 2
+    qo = 2 * w.B * w.H * w.N * w.d * elem
+    kv = 0
+    for b in range(w.B):
+        L = w.N if key_len is None else int(min(max(key_len[b], 0), w.N))
+        kv += 2 * w.H * L * w.d * elem
+    return qo + kv + w.B * w.H * w.N * 4
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest()
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"\s*traffic\s+(.*)$", line)
+        if not m:
+            continue
+        kv = dict(x.split("=", 1) for x in m.group(1).split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload \
+                and kv.get("source_sha256_16") == digest:
+            return int(float(kv["hbm_bytes_per_launch"]))
+    return None
+
+
+def copy_probe():
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES,
+                      "copy_probe_bytes_written": COPY_PROBE_BYTES, "launches": 5}))
+
+
+def cpu_baseline(w, case, target_s: float):
+    """Time the fp64 oracle on a bounded sample of the workload's query rows."""
+    import attn_inputs as ai
+    import oracle
+    dt = case["dtype"]
+    Q = ai.bits_to_f32(case["Q"], dt)
+    K = ai.bits_to_f32(case["K"], dt)
+    V = ai.bits_to_f32(case["V"], dt)
+    kl = case["key_len"]
+    rng = np.random.Generator(np.random.PCG64(w.seed + 31))
+
+    def rows_flops(sel):
+        f = 0
+        for b, h, i in sel:
+            L = w.N if kl is None else int(min(max(kl[b], 0), w.N))
+            n = min(L, i + 1) if w.causal else L
+            f += 4 * w.d * n
+        return f
+
+    def pick(per_head):
+        out = []
+        for b in range(w.B):
+            for h in range(w.H):
+                for i in rng.choice(w.N, size=per_head, replace=False):
+                    out.append((b, h, int(i)))
+        return np.asarray(out, np.int64)
+
+    sel = pick(2)
+    t0 = time.perf_counter()
+    oracle.sdpa_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    rate = rows_flops(sel) / max(time.perf_counter() - t0, 1e-6)
+    per_row = 4 * w.d * (w.N / 2 if w.causal else w.N)
+    per_head = int(max(1, min(w.N, target_s * rate / per_row / (w.B * w.H))))
+    sel = pick(per_head)
+    flops = rows_flops(sel)
+    t0 = time.perf_counter()
+    oracle.sdpa_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    secs = time.perf_counter() - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{per_head} seeded random query rows per (b,h) of all {w.B * w.H} heads, "
+                      f"each over its full visible key range; {flops:.3e} flops in {secs:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); attention heads "
+              "shard across GPUs without any exchange, so the multi-GPU figure is N "
+              "times this one-GPU throughput and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+    import attn_inputs as ai
+    import exact_self_attention_amd as attn
+
+    w = ai.WORKLOADS[args.workload]
+    case = ai.generate(w)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+        return t.view(torch.float16 if w.dtype == ai.F16 else torch.bfloat16)
+
+    q, k, v = to_dev(case["Q"]), to_dev(case["K"]), to_dev(case["V"])
+    kl = None if case["key_len"] is None else torch.from_numpy(case["key_len"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = float(w.scale)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    F = metric_flops(w)
+    key_len = case["key_len"]
+    pairs = visible_pairs(w, key_len)
+    F_alg = 4.0 * w.d * pairs
+    kernel = attn.attn_fwd_kernel_name(attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16,
+                                       w.d, w.N, w.causal, key_len is not None)
+    if w.key_padding:
+        nbytes = algorithmic_bytes(w, key_len)
+        achieved = nbytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = F_alg / launch_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["traffic"] = read_traffic(kernel, w.name)
+    roof["kernel"] = kernel
+    roof["avg_launch_us"] = launch_s * 1e6
+
+    value = F / (ms_per_step / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "key_padding": w.key_padding, "seed": w.seed,
+                   "global_batch": w.B, "seq_len": w.N},
+        "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+"""Python binding of libattn.so, the gfx950 exact-attention forward library.
+
+Argument marshalling only: every function here checks what ctypes cannot
+(tensor dtype, device, contiguity), passes raw device pointers, sizes and the
+current HIP stream to the C function of the same name, and turns a non-zero
+status into ``AttnError``.  All arithmetic runs in the HIP kernels.  PyTorch
+supplies device memory and streams.
+
+Importing this package raises ImportError when libattn.so has not been built
+(``python -m exact_self_attention_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+          3: "ATTN_ERR_MISALIGNED", 4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH",
+          6: "ATTN_ERR_DEVICE"}
+EXPORTS = ["attn_fwd", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
+           "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({attn_status_string(status)})")
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "'python -m exact_self_attention_amd.build' (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    common = [i32, p, p, p, p, p, i64, i64, i64, i64, f32, i32, p]
+    lib.attn_fwd.argtypes = common + [p]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_naive.argtypes = common + [p, ctypes.c_size_t, p]
+    lib.attn_fwd_naive.restype = i32
+    lib.attn_fwd_naive_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_fwd_naive_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_fwd_kernel_name.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, ctypes.c_size_t]
+    lib.attn_fwd_kernel_name.restype = i32
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"dtype {t.dtype} is not float16 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensors(q, k, v, o, lse, key_len):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    if not q.is_cuda:
+        raise ValueError("tensors must live on a GPU")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) \
+                or not lse.is_contiguous() or lse.device != q.device:
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or tuple(key_len.shape) != (q.shape[0],) \
+                or not key_len.is_contiguous() or key_len.device != q.device:
+            raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
+
+
+def attn_fwd(q, k, v, o, lse=None, *, scale: float, causal: bool = False,
+             key_len=None, stream=None) -> None:
+    """Fused forward: writes o (and lse when given).  See include/attn.h."""
+    code = _dtype_code(q)
+    _check_tensors(q, k, v, o, lse, key_len)
+    B, H, N, d = q.shape
+    st = lib.attn_fwd(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                      B, H, N, d, float(scale), int(bool(causal)), _ptr(key_len),
+                      _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd", st)
+
+
+def attn_fwd_naive(q, k, v, o, lse=None, *, workspace: torch.Tensor, scale: float,
+                   causal: bool = False, key_len=None, stream=None) -> None:
+    """Unfused baseline (materialises S and P in ``workspace``)."""
+    code = _dtype_code(q)
+    _check_tensors(q, k, v, o, lse, key_len)
+    B, H, N, d = q.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_naive(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            B, H, N, d, float(scale), int(bool(causal)), _ptr(key_len),
+                            _ptr(workspace), nbytes, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_naive", st)
+
+
+def attn_fwd_naive_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib.attn_fwd_naive_workspace_bytes(B, H, N))
+
+
+def attn_status_string(status: int) -> str:
+    return lib.attn_status_string(int(status)).decode()
+
+
+def attn_fwd_kernel_name(dtype: int, d: int, N: int, causal: bool, has_key_len: bool) -> str:
+    buf = ctypes.create_string_buffer(128)
+    st = lib.attn_fwd_kernel_name(dtype, d, N, int(bool(causal)), int(bool(has_key_len)), buf, 128)
+    if st != 0:
+        raise AttnError("attn_fwd_kernel_name", st)
+    return buf.value.decode()
+
+
+def attn_version() -> int:
+    return int(lib.attn_version())
+
+
+def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, key_len=None,
+        want_lse: bool = True, stream=None):
+    """Allocate O (and LSE) with torch and run attn_fwd; returns (o, lse)."""
+    if scale is None:
+        scale = float(torch.tensor(1.0 / q.shape[-1] ** 0.5, dtype=torch.float32))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    attn_fwd(q, k, v, o, lse, scale=scale, causal=causal, key_len=key_len, stream=stream)
+    return o, lse

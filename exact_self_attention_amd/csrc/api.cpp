@@ -1,0 +1,196 @@
+// C ABI of libattn.so (declared in include/attn.h): argument checks,
+// dispatch to a kernel instance, launch on the caller's stream.
+//
+// Every argument check runs before any HIP runtime call, so a rejected call
+// never touches the device.  Nothing here allocates device memory.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int kMaxDevices = 64;
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Checks shared by attn_fwd and attn_fwd_naive.  *empty is set when there is
+// nothing to compute (B*H*N == 0).
+attn_status_t check_args(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                         const void *O, const float *LSE, int64_t B, int64_t H, int64_t N,
+                         int64_t d, float scale, const int32_t *key_len, bool *empty) {
+    *empty = false;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_INVALID_ARG;
+    if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (N > kMaxN) return ATTN_ERR_INVALID_ARG;
+    if (B > 0 && H > INT32_MAX / B) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || N == 0) {
+        *empty = true;
+        return ATTN_OK;
+    }
+    if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+        return ATTN_ERR_MISALIGNED;
+    if (!aligned(LSE, 4) || !aligned(key_len, 4)) return ATTN_ERR_MISALIGNED;
+    const size_t elems = (size_t)B * (size_t)H * (size_t)N;
+    const size_t tbytes = elems * (size_t)d * 2;
+    const size_t lbytes = elems * sizeof(float);
+    const size_t kbytes = (size_t)B * sizeof(int32_t);
+    if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) ||
+        overlaps(O, tbytes, V, tbytes))
+        return ATTN_ERR_INVALID_ARG;
+    if (LSE != nullptr &&
+        (overlaps(LSE, lbytes, Q, tbytes) || overlaps(LSE, lbytes, K, tbytes) ||
+         overlaps(LSE, lbytes, V, tbytes) || overlaps(LSE, lbytes, O, tbytes)))
+        return ATTN_ERR_INVALID_ARG;
+    if (key_len != nullptr &&
+        (overlaps(key_len, kbytes, O, tbytes) || overlaps(key_len, kbytes, LSE, lbytes)))
+        return ATTN_ERR_INVALID_ARG;
+    return ATTN_OK;
+}
+
+// The current device must be a gfx950; checked once per device.
+attn_status_t check_device() {
+    static std::atomic<int> state[kMaxDevices];  // 0 unknown, 1 ok, 2 bad
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int s = state[dev].load(std::memory_order_relaxed);
+        if (s != 0) return s == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(attn_dtype_t dtype, const void *Q, const void *K, const void *V, void *O,
+                       float *LSE, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       int causal, const int32_t *key_len, void *stream) {
+    bool empty = false;
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    if (st != ATTN_OK || empty) return st;
+    st = check_device();
+    if (st != ATTN_OK) return st;
+    attn::FwdParams p;
+    p.Q = static_cast<const uint16_t *>(Q);
+    p.K = static_cast<const uint16_t *>(K);
+    p.V = static_cast<const uint16_t *>(V);
+    p.O = static_cast<uint16_t *>(O);
+    p.LSE = LSE;
+    p.key_len = key_len;
+    p.N = N;
+    p.BH = (int)(B * H);
+    p.H = (int)H;
+    p.n_qtiles = 0;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    const hipError_t e = attn::launch_fwd(dtype == ATTN_BF16, (int)d, causal != 0, p,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                             void *O, float *LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                             float scale, int causal, const int32_t *key_len, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    bool empty = false;
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((N + 15) / 16 > 65535) return ATTN_ERR_INVALID_ARG;  // grid limit of the score kernel
+    const size_t per_head = attn_fwd_naive_workspace_bytes(1, 1, N);
+    if (per_head == 0) return ATTN_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < per_head) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_MISALIGNED;
+    const size_t elems = (size_t)B * (size_t)H * (size_t)N;
+    if (overlaps(workspace, workspace_bytes, Q, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, K, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, V, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, O, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, LSE, LSE ? elems * 4 : 0) ||
+        overlaps(workspace, workspace_bytes, key_len, key_len ? (size_t)B * 4 : 0))
+        return ATTN_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != ATTN_OK) return st;
+
+    const int BH = (int)(B * H);
+    size_t group = workspace_bytes / per_head;
+    if (group > 65535) group = 65535;  // grid limit of the head dimension
+    attn::NaiveParams p;
+    p.Q = static_cast<const uint16_t *>(Q);
+    p.K = static_cast<const uint16_t *>(K);
+    p.V = static_cast<const uint16_t *>(V);
+    p.O = static_cast<uint16_t *>(O);
+    p.LSE = LSE;
+    p.key_len = key_len;
+    p.S = static_cast<float *>(workspace);
+    p.N = N;
+    p.d = (int)d;
+    p.H = (int)H;
+    p.scale = scale;
+    p.causal = causal != 0;
+    p.bf16 = dtype == ATTN_BF16;
+    for (int bh0 = 0; bh0 < BH; bh0 += (int)group) {
+        p.bh0 = bh0;
+        p.nbh = (int)((size_t)(BH - bh0) < group ? (size_t)(BH - bh0) : group);
+        if (attn::launch_naive(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    return ATTN_OK;
+}
+
+size_t attn_fwd_naive_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    if (B < 0 || H < 0 || N < 0 || N > kMaxN) return 0;
+    const unsigned __int128 total = (unsigned __int128)B * (unsigned __int128)H *
+                                    (unsigned __int128)N * (unsigned __int128)N * 4u;
+    if (total > (unsigned __int128)SIZE_MAX) return 0;
+    return (size_t)total;
+}
+
+const char *attn_status_string(attn_status_t status) {
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (size, scale, null pointer or aliasing)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype (d must be 32, 64 or 128)";
+    case ATTN_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, LSE and key_len 4)";
+    case ATTN_ERR_WORKSPACE: return "naive workspace missing or smaller than one head's N*N*4 bytes";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
+    }
+    return "unknown status";
+}
+
+attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N, int causal,
+                                   int has_key_len, char *buf, size_t buf_len) {
+    (void)has_key_len;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (N < 0 || N > kMaxN) return ATTN_ERR_INVALID_ARG;
+    if (buf == nullptr || buf_len == 0) return ATTN_ERR_INVALID_ARG;
+    std::snprintf(buf, buf_len, "%s", attn::fwd_kernel_name(dtype == ATTN_BF16, (int)d, causal != 0));
+    return ATTN_OK;
+}
+
+int attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C ABI (api.cpp) and the gfx950 kernels.
+// Not installed; the public interface is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments of one fused forward launch.  All pointers are device pointers;
+// 16-bit tensors are passed as raw bit patterns.
+struct FwdParams {
+    const uint16_t *Q, *K, *V;  // [B, H, N, d]
+    uint16_t *O;                // [B, H, N, d]
+    float *LSE;                 // [B, H, N] or nullptr
+    const int32_t *key_len;     // [B] or nullptr
+    int64_t N;
+    int BH;                     // B * H
+    int H;
+    int n_qtiles;               // ceil(N / query rows per workgroup)
+    float scale_log2;           // scale * log2(e)
+};
+
+// Query rows each fused workgroup owns (the query tile height).
+int fwd_query_tile(int d);
+// Launches the fused kernel instance for (bf16, d, causal).  p.n_qtiles is
+// filled in here.
+hipError_t launch_fwd(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
+// Name of that instance, as profilers report it.
+const char *fwd_kernel_name(bool bf16, int d, bool causal);
+
+// Arguments of the unfused baseline, for heads [bh0, bh0 + nbh).
+struct NaiveParams {
+    const uint16_t *Q, *K, *V;
+    uint16_t *O;
+    float *LSE;
+    const int32_t *key_len;
+    float *S;                   // nbh * N * N fp32 scores, then probabilities
+    int64_t N;
+    int d;
+    int H;
+    int bh0;
+    int nbh;
+    float scale;
+    int causal;
+    int bf16;
+};
+
+hipError_t launch_naive(const NaiveParams &p, hipStream_t s);
+
+}  // namespace attn

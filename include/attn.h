@@ -1,0 +1,145 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact scaled-dot-product attention
+ * forward library, libattn.so.
+ *
+ * Operation (every entry point computes the same thing):
+ *
+ *   O = softmax(scale * Q K^T + mask) V,   LSE = log of the softmax normaliser
+ *
+ * over tensors laid out as [B, H, N, d].  This is the attention of "Tensor
+ * Parallelism with CUDA - Standard Attention" (S = Q K^T / sqrt(d), row-wise
+ * softmax, O = P V) with the scale as an argument, and the masked five-step
+ * form of "Naive Attention Kernel" (section 1), where the mask here is
+ * structural (masked keys get probability exactly 0):
+ *
+ *   - key padding: per sequence b a valid key length L_b; keys j >= L_b are
+ *     masked (the key-side mask of "cuda-reranker");
+ *   - causal: key j is visible to query i only when j <= i (equal query and
+ *     key lengths, top-left aligned).
+ *
+ * For each (b, h, i):  S_ij = scale * (q_i . k_j) over visible keys j,
+ *   LSE_i = log(sum_j exp(S_ij)),  O_i = sum_j exp(S_ij - LSE_i) v_j.
+ * A row with no visible key gets O_i = 0 and LSE_i = -inf.
+ *
+ * Conventions common to all entry points
+ * --------------------------------------
+ *  dtype    ATTN_F16 (IEEE binary16) or ATTN_BF16 (bfloat16) for Q, K, V and
+ *           O.  Arithmetic is fp32 on the GPU (fp16/bf16 matrix-core inputs,
+ *           fp32 accumulation); O is rounded to nearest-even into dtype.
+ *  layout   Q, K, V, O: contiguous row-major [B, H, N, d] device arrays,
+ *           16-byte aligned.  LSE: contiguous fp32 [B, H, N] device array,
+ *           4-byte aligned, or NULL when not wanted.
+ *  sizes    B, H, N >= 0; d in {32, 64, 128}.  B*H*N == 0 is a no-op.
+ *           B*H <= 2^31 - 1 and N <= 2^30.
+ *  scale    finite and >= 0 (normally 1/sqrt(d)).
+ *  key_len  NULL (no padding mask) or a device int32 array [B]; values are
+ *           clamped to [0, N] on the device.  K and V rows j >= L_b are never
+ *           read, so they may hold anything (including NaN).
+ *  stream   a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *           enqueued asynchronously; the call does not synchronise.
+ *  ownership  the caller owns every buffer.  The library allocates no device
+ *           memory, keeps no per-call state, and caches only device
+ *           properties.  Calls are reentrant; calls on different streams may
+ *           run concurrently.
+ *  aliasing O and LSE must not overlap Q, K, V, key_len or each other.
+ *  errors   argument errors are returned synchronously before anything is
+ *           enqueued; ATTN_ERR_LAUNCH reports a failed kernel launch.  Faults
+ *           inside a kernel surface at the caller's next synchronisation.
+ *  determinism  identical inputs give bitwise identical outputs.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F16 = 0,
+    ATTN_BF16 = 1
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,  /* bad size, scale, pointer or aliasing */
+    ATTN_ERR_UNSUPPORTED = 2,  /* d not in {32, 64, 128} or unknown dtype */
+    ATTN_ERR_MISALIGNED = 3,   /* a pointer is not aligned as required */
+    ATTN_ERR_WORKSPACE = 4,    /* naive workspace missing or too small */
+    ATTN_ERR_LAUNCH = 5,       /* the HIP runtime rejected a launch */
+    ATTN_ERR_DEVICE = 6        /* no usable gfx950 device is current */
+} attn_status_t;
+
+/*
+ * attn_fwd -- fused, tiled forward pass.
+ *
+ * One kernel launch.  Each workgroup owns a tile of query rows of one (b, h),
+ * keeps them in registers, streams the visible key/value tiles through LDS,
+ * and keeps a running row maximum, running normaliser and rescaled output
+ * accumulator (the online-softmax recurrence of "Self-Attention Kernel &
+ * Inference Engine from Scratch", section "Online Softmax Formulation"), so
+ * the N x N score matrix never reaches device memory.  Key tiles that are
+ * wholly masked (past L_b, or after the query tile under causal masking) are
+ * skipped (same page, "Engineering Decisions & Trade-offs"; "cuda-reranker",
+ * the padding tile skip).
+ *
+ * Q, K, V: inputs as above.  O: output [B, H, N, d] in dtype.  LSE: optional
+ * fp32 output [B, H, N] (natural log).  Returns ATTN_OK or an error code.
+ */
+attn_status_t attn_fwd(attn_dtype_t dtype,
+                       const void *Q, const void *K, const void *V,
+                       void *O, float *LSE,
+                       int64_t B, int64_t H, int64_t N, int64_t d,
+                       float scale, int causal, const int32_t *key_len,
+                       void *stream);
+
+/*
+ * attn_fwd_naive -- unfused baseline that materialises scores and
+ * probabilities ("Naive Attention Kernel", sections 1 and 3; "Tensor
+ * Parallelism with CUDA - Standard Attention", sections "Why This
+ * Ordering?" and "The Naive HBM Algorithm").
+ *
+ * Three launches per group of heads: scores S = scale Q K^T (fp32, masked
+ * entries -inf) written to the workspace; a row-wise softmax in place
+ * (max, exponential sum, normalise; also writes LSE); then O = P V.
+ * workspace: device memory of workspace_bytes, 16-byte aligned, owned by the
+ * caller and overwritten.  It must hold at least one head's fp32 N x N matrix
+ * (attn_fwd_naive_workspace_bytes(1, 1, N)); with less than
+ * attn_fwd_naive_workspace_bytes(B, H, N) the heads are processed in groups.
+ * Returns ATTN_ERR_WORKSPACE when the workspace is NULL or too small.
+ */
+attn_status_t attn_fwd_naive(attn_dtype_t dtype,
+                             const void *Q, const void *K, const void *V,
+                             void *O, float *LSE,
+                             int64_t B, int64_t H, int64_t N, int64_t d,
+                             float scale, int causal, const int32_t *key_len,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Bytes of workspace that let attn_fwd_naive process all B*H heads at once:
+ * B * H * N * N * 4.  Returns 0 for negative sizes or on overflow. */
+size_t attn_fwd_naive_workspace_bytes(int64_t B, int64_t H, int64_t N);
+
+/* Static, NUL-terminated description of a status code. */
+const char *attn_status_string(attn_status_t status);
+
+/*
+ * Name of the kernel instance attn_fwd launches for these arguments (for
+ * profilers), written into buf (NUL-terminated, truncated to buf_len).
+ * Returns the same status attn_fwd would return for an argument error,
+ * else ATTN_OK.  Touches no device state.
+ */
+attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N,
+                                   int causal, int has_key_len,
+                                   char *buf, size_t buf_len);
+
+/* Library ABI version (major * 100 + minor). */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,188 @@
+"""GPU parity: the HIP entry points, called through the C ABI, against the fp64
+oracle on the same seeded inputs, and against closed forms at full size."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+ROWS_PER_HEAD = {"single_head": None, "reranker": None, "prefill": 48,
+                 "peaky": 32, "long_context": None}
+
+
+def _selection(w, case):
+    if w.name == "long_context":
+        return ai.sampled_rows_selection(case["rows"], w.B)
+    if ROWS_PER_HEAD[w.name] is None:
+        return ai.all_rows_selection(w.B, w.H, w.N)
+    return gu.sample_rows(w.B, w.H, w.N, ROWS_PER_HEAD[w.name], seed=w.seed + 7)
+
+
+@pytest.fixture(scope="module")
+def cases():
+    return {}
+
+
+def _case(cases, name):
+    if name not in cases:
+        w = ai.WORKLOADS[name]
+        gu.log(f"generating {name} {w.shape} {w.dtype} seed={w.seed}")
+        cases[name] = ai.generate(w)
+    return cases[name]
+
+
+@pytest.mark.parametrize("name", ai.WORKLOAD_ORDER)
+def test_fused_matches_oracle_on_workload(cases, name):
+    w = ai.WORKLOADS[name]
+    case = _case(cases, name)
+    gu.log(f"fused parity {name} {w.shape} {w.dtype} causal={w.causal}")
+    O, LSE = gu.run_fused(case, w.causal)
+    sel = _selection(w, case)
+    O_ref, LSE_ref = gu.oracle_rows(case, w.causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"fused/{name}", sel)
+    assert np.all(np.isfinite(O))
+
+
+@pytest.mark.parametrize("name", ["single_head", "reranker", "prefill", "peaky"])
+def test_naive_matches_oracle_on_workload(cases, name):
+    w = ai.WORKLOADS[name]
+    case = _case(cases, name)
+    gu.log(f"naive parity {name}")
+    O, LSE = gu.run_naive(case, w.causal)
+    sel = _selection(w, case)
+    O_ref, LSE_ref = gu.oracle_rows(case, w.causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"naive/{name}", sel)
+
+
+def test_naive_in_head_groups_matches_full_workspace(cases):
+    w = ai.WORKLOADS["reranker"]
+    case = _case(cases, "reranker")
+    O1, L1 = gu.run_naive(case, w.causal)
+    O2, L2 = gu.run_naive(case, w.causal, max_workspace_bytes=7 * 256 * 256 * 4)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+FUZZ_N = [1, 2, 17, 48, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 1000]
+FUZZ = []
+for _n in FUZZ_N:
+    for _d in (32, 64, 128):
+        for _causal in (False, True):
+            FUZZ.append((_n, _d, _causal))
+
+
+@pytest.mark.parametrize("N,d,causal", FUZZ, ids=[f"N{n}-d{d}-{'c' if c else 'f'}" for n, d, c in FUZZ])
+def test_fuzz_shapes(N, d, causal):
+    dtype = ai.BF16 if (N + d) % 2 else ai.F16
+    seed = 10_000 + N * 7 + d * 3 + causal
+    # key lengths cover 0, 1, N-1, N and a random value
+    B = 5
+    kl = [0, 1, max(N - 1, 0), N, int(np.random.default_rng(seed).integers(0, N + 1))]
+    case = ai.random_case(B, 2, N, d, dtype, seed=seed, sigma=1.5, key_len=kl)
+    gu.log(f"fuzz N={N} d={d} causal={causal} {dtype} key_len={kl}")
+    O, LSE = gu.run_fused(case, causal)
+    sel = ai.all_rows_selection(B, 2, N)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"fuzz N={N} d={d} causal={causal}", sel)
+    # no key-length array: every key visible
+    case["key_len"] = None
+    O, LSE = gu.run_fused(case, causal)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"fuzz-nomask N={N} d={d}", sel)
+
+
+@pytest.mark.parametrize("name", ["prefill", "long_context"])
+def test_zero_query_gives_prefix_means_every_row(name):
+    """Q = 0 under causal masking: O_i is the mean of V_0..V_i and LSE_i = ln(i+1),
+    checked on every row at the full workload size."""
+    w = ai.WORKLOADS[name]
+    gu.log(f"zero-query closed form {name}")
+    rng = np.random.Generator(np.random.PCG64(w.seed + 100))
+    vbits = ai.round_bits(rng.standard_normal(size=w.shape, dtype=np.float32), w.dtype)
+    qbits = np.zeros(w.shape, np.uint16)
+    kbits = ai.round_bits(rng.standard_normal(size=w.shape, dtype=np.float32), w.dtype)
+    case = {"Q": qbits, "K": kbits, "V": vbits, "dtype": w.dtype, "scale": w.scale, "key_len": None}
+    O, LSE = gu.run_fused(case, True)
+    del kbits, qbits
+    atol, rtol = gu.TOL[w.dtype]
+    V = ai.bits_to_f32(vbits, w.dtype)
+    n = np.arange(1, w.N + 1, dtype=np.float64)[:, None]
+    for h in range(w.H):
+        ref = np.cumsum(V[0, h].astype(np.float64), axis=0) / n
+        err = np.abs(O[0, h] - ref)
+        assert np.all(err <= atol + rtol * np.abs(ref)), (h, float(err.max()))
+        assert np.all(np.abs(LSE[0, h] - np.log(n[:, 0])) <= gu.LSE_TOL), h
+
+
+def test_causal_row_zero_is_exact():
+    w = ai.WORKLOADS["prefill"]
+    case = ai.generate(w)
+    O, LSE = gu.run_fused(case, True)
+    V = ai.bits_to_f32(case["V"], w.dtype)
+    assert np.array_equal(O[:, :, 0], V[:, :, 0])
+
+
+def test_padding_rows_are_never_read():
+    """NaN in K and V rows at or past each key length leaves O and LSE unchanged."""
+    case = ai.random_case(4, 3, 300, 64, ai.F16, seed=77, key_len=[0, 1, 130, 299])
+    O1, L1 = gu.run_fused(case, False)
+    nan16 = np.uint16(0x7E00)
+    for b, L in enumerate(case["key_len"]):
+        case["K"][b, :, L:] = nan16
+        case["V"][b, :, L:] = nan16
+    O2, L2 = gu.run_fused(case, False)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    assert np.all(np.isfinite(O2))
+    assert np.all(O2[0] == 0) and np.all(np.isneginf(L2[0]))
+
+
+def test_key_len_one_returns_first_value_row():
+    case = ai.random_case(2, 2, 200, 128, ai.BF16, seed=78, key_len=[1, 1])
+    for causal in (False, True):
+        O, LSE = gu.run_fused(case, causal)
+        V = ai.bits_to_f32(case["V"], ai.BF16)
+        for i in (0, 5, 199):
+            assert np.array_equal(O[:, :, i], V[:, :, 0])
+
+
+def test_bitwise_deterministic():
+    w = ai.WORKLOADS["peaky"]
+    case = ai.generate(w)
+    inputs = gu.dev_inputs(case)
+    O1, L1 = gu.run_fused(case, w.causal, inputs)
+    O2, L2 = gu.run_fused(case, w.causal, inputs)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_slices_are_independent():
+    """Changing one (b, h) slice leaves every other slice bitwise equal."""
+    case = ai.random_case(2, 3, 257, 32, ai.F16, seed=79)
+    O1, L1 = gu.run_fused(case, True)
+    case["K"][1, 2] = ai.round_bits(np.full((257, 32), 0.5, np.float32), ai.F16)
+    O2, L2 = gu.run_fused(case, True)
+    keep = np.ones((2, 3), bool)
+    keep[1, 2] = False
+    assert np.array_equal(O1[keep], O2[keep]) and np.array_equal(L1[keep], L2[keep])
+    assert not np.array_equal(O1[1, 2], O2[1, 2])
+
+
+def test_output_written_only_inside_bounds():
+    """Canaries around O and LSE survive a launch whose N is not a tile multiple."""
+    case = ai.random_case(1, 2, 131, 128, ai.F16, seed=80)
+    q, k, v, _ = gu.dev_inputs(case)
+    import exact_self_attention_amd as attn
+    n_o = q.numel()
+    buf = torch.full((n_o + 2048,), -7.0, dtype=torch.float16, device=q.device)
+    o = buf[1024:1024 + n_o].view(q.shape)
+    lbuf = torch.full((2 * 131 + 128,), 3.5, dtype=torch.float32, device=q.device)
+    lse = lbuf[64:64 + 2 * 131].view(1, 2, 131)
+    attn.attn_fwd(q, k, v, o, lse, scale=float(case["scale"]), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:1024] == -7.0) and torch.all(buf[1024 + n_o:] == -7.0)
+    assert torch.all(lbuf[:64] == 3.5) and torch.all(lbuf[64 + 2 * 131:] == 3.5)
