@@ -1,37 +1,44 @@
 // Fused exact attention forward for gfx950 (CDNA4).
 //
-// One workgroup = 4 waves = one tile of 128 query rows of one (b, h); each
-// wave owns 32 query rows.  Per key tile of 64 rows:
+// One workgroup = 8 waves = one tile of 256 query rows of one (b, h); each
+// wave owns 32 query rows.  Key/value tiles of 64 rows stream through LDS.
+// Per key tile j, each wave computes
 //
-//   S^T = K_j Q_i^T          on 32x32x16 MFMA (fp16/bf16 in, fp32 out)
-//   online softmax update    running max m, running sum l, rescale of O
-//   O^T += V_j^T P^T         on 32x32x16 MFMA, P taken straight from the
-//                            S^T accumulators (no LDS round trip)
+//   S^T = K_j Q^T            32x32x16 MFMA, fp16/bf16 in, fp32 out
+//   online softmax update    running max m, running sum l, O rescale
+//   O^T += V_j^T P^T         32x32x16 MFMA, P taken from the S^T registers
 //
-// This is the tiled online-softmax forward of "Self-Attention Kernel &
+// which is the tiled online-softmax forward of "Self-Attention Kernel &
 // Inference Engine from Scratch" (sections "Online Softmax Formulation" and
-// "CUDA Kernel Structure"): the running max/normaliser merge of two score
-// blocks, the output rescaled by exp(m_old - m_new), and the division by the
-// normaliser deferred to the end.  The design here is gfx950-specific:
+// "CUDA Kernel Structure"): two score blocks merge through the running max
+// and normaliser, the output is rescaled by exp(m_old - m_new), and the
+// division by the normaliser is deferred to the end.  The gfx950 design:
 //
-//  * Computing S^T (keys as MFMA rows, queries as columns) puts one query's
-//    scores in one lane: a row max / row sum is 16 in-lane values per 32-key
-//    block plus one exchange with the lane 32 away.
+//  * Two wave groups ping-pong.  Waves 0-3 and 4-7 sit on the four SIMDs in
+//    pairs.  Phases are separated by workgroup barriers; in every phase one
+//    group issues matrix-core work (P.V of the previous tile and Q.K of the
+//    current one) while the other runs the softmax of its current tile on
+//    the vector ALU, so each SIMD keeps its matrix core and its VALU busy at
+//    the same time.
+//  * S^T (keys as MFMA rows, queries as columns) keeps one query's scores in
+//    one lane: a row max or sum is in-lane work plus one exchange with the
+//    lane 32 away (v_permlane32_swap).
 //  * The S^T accumulator layout (lane = query + 32*g, register r = key
-//    8*(r/4) + 4*g + r%4) is consumed as the B operand of the P.V MFMA
-//    as-is; V is stored transposed in LDS with keys permuted inside each
-//    group of 16 so that lane group g reads its 8 keys with one 128-bit LDS
-//    load.  The sum over keys does not care about the order; masks use the
-//    true key index.
-//  * Q stays in VGPRs for the whole loop.  K and V tiles are double
-//    buffered in LDS, and the next tile's global loads (128-bit, coalesced)
-//    are in flight while the current tile is computed.
-//  * Exponentials use exp2 with scale*log2(e) folded into one FMA.
+//    8*(r/4) + 4*g + r%4) is used as the B operand of the P.V MFMA as it
+//    is.  V is stored transposed in LDS with keys permuted inside each group
+//    of 16 so that lane group g reads its 8 keys with one 128-bit load.
+//  * K is stored row-major with 16-byte chunks XOR-swizzled by row, so the
+//    128-bit fragment reads of 8 or 16 consecutive rows hit distinct banks.
+//  * Q stays in VGPRs.  Global loads of the tiles two phases ahead are in
+//    flight while the current ones are used (register staging, then LDS).
+//  * exp2 with scale*log2(e) folded into one FMA; the running max is only
+//    raised when a tile's max exceeds it by more than 2^8 (lazy rescale):
+//    the result is the same, probabilities stay below 256.
 //  * Causal and key-padding masks: the loop stops at the last key tile any
-//    row of the workgroup can see; whole-tile skip per wave on the causal
-//    diagonal; per-element masking only on tiles that straddle a boundary.
-//    Key rows past the valid length are never read (loaded as zeros).
-//  * Causal grids launch the heaviest query tiles first.
+//    row of the workgroup can see, each wave skips tiles wholly after its
+//    rows, per-element masking only on tiles that straddle a boundary, and
+//    key rows past the valid length are never read.  Causal grids launch
+//    the heaviest query tiles first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,13 +57,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kQRows = 32;               // query rows per wave
 constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.0f;            // log2 of the largest unscaled probability
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -80,6 +87,15 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Value of x in the lane 32 away (lanes l and l^32 swap).
+__device__ __forceinline__ float other_half(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // r[0] holds the low half of the wave twice, r[1] the high half twice.
+    const uint32_t lo = r[0], hi = r[1];
+    return __builtin_bit_cast(float, (__lane_id() < 32) ? hi : lo);
+}
+
 // Position of key k (0..kBN-1) inside a transposed V tile row.  Within each
 // group of 16 keys the order is 0-3, 8-11, 4-7, 12-15, so that the 8 keys a
 // lane group holds in the S^T accumulator (4g..4g+3 and 8+4g..8+4g+3) are
@@ -94,31 +110,42 @@ __device__ __forceinline__ uint32_t half_of(u32x4 v, int e) {
     return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// XOR swizzle of the 16-byte chunk index of K tile row `row` (D halves per
+// row): rows that share a 256-byte bank window get distinct chunk offsets.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    constexpr int RP = 128 / D;  // rows per 256 bytes
+    constexpr int CPR = D / 8;   // chunks per row
+    return (row / RP) % CPR;
+}
+
 template <int D, bool BF16, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
-    constexpr int KSTR = D + 8;          // LDS row stride of a K tile (halves)
-    constexpr int VSTR = kBN + 8;        // LDS row stride of a V^T tile
-    constexpr int KTILE = kBN * KSTR;
+    constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    constexpr int KTILE = kBN * D;                // halves per K tile (no padding)
+    constexpr int VSTR = kBN + 8;                 // LDS row stride of a V^T tile
     constexpr int VTILE = D * VSTR;
-    constexpr int STAGE = KTILE + VTILE;
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int K_RPP = kThreads / CPR;
-    constexpr int K_PASSES = kBN / K_RPP;
-    constexpr int KG = kBN * D / (8 * kThreads);  // keys per thread, V load
-    constexpr int KB = kBN / 32;         // 32-key blocks per tile
-    constexpr int DK = D / 16;           // 16-deep k-steps of Q.K
-    constexpr int DB = D / 32;           // 32-wide column blocks of O
-    static_assert(K_PASSES * K_RPP == kBN, "K tile load shape");
+    constexpr int K_CHUNKS = kBN * CPR;
+    constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
+    constexpr int KG_RAW = kBN * D / (8 * kThreads);
+    constexpr int KG = KG_RAW >= 1 ? KG_RAW : 1;  // keys per thread in a V tile load
+    constexpr int V_ITEMS = (kBN / KG) * CPR;
+    constexpr int KB = kBN / 32;                  // 32-key blocks per tile
+    constexpr int DK = D / 16;                    // 16-deep k-steps of Q.K
+    constexpr int DB = D / 32;                    // 32-wide column blocks of O
     static_assert(KG == 1 || KG == 2 || KG == 4, "V tile load shape");
-    static_assert((kBN / KG) * CPR == kThreads, "V tile load shape");
+    static_assert(V_ITEMS <= kThreads, "V tile load shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * KTILE + 2 * VTILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
+    const int grp = wave >> 2;       // ping-pong group
+    const int simd = wave & 3;
+    const int rb = 2 * simd + grp;   // this wave's 32-row block in the tile
 
     const int BH = p.BH;
     const int bh = blockIdx.x % BH;
@@ -139,10 +166,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int q0 = qt * kBM;
     int kv_end = Lk;
     if (CAUSAL) kv_end = min(kv_end, q0 + kBM);
-    const int n_tiles = (kv_end + kBN - 1) / kBN;
-    const int qw0 = q0 + wave * kQRows;
+    const int n = (kv_end + kBN - 1) / kBN;       // key tiles of the workgroup
+    const int qw0 = q0 + rb * kQRows;
     const int my_q = qw0 + l32;
     const bool q_ok = my_q < N;
+    int n_w = n;                                  // key tiles this wave computes
+    if (CAUSAL) n_w = (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN;
+    if (qw0 >= N) n_w = 0;
 
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     u32x4 qf[DK];
@@ -151,155 +181,193 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         qf[kk] = q_ok ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + kk * 16 + g * 8)
                       : zero4;
 
-    u32x4 kreg[K_PASSES];
-    u32x4 vreg[KG];
-    const int ld_ch = tid % CPR;
-    const int ld_row = tid / CPR;
+    // ---- tile loads: global -> staging registers -> LDS
+    u32x4 stg_k[K_PER_T];
+    u32x4 stg_v[KG];
+    const int v_ch = tid % CPR;
+    const int v_grp = tid / CPR;
 
-    auto gload = [&](int t) {
-        const int j0 = t * kBN;
+    auto gload = [&](int tk, int tv) {
 #pragma unroll
-        for (int ps = 0; ps < K_PASSES; ++ps) {
-            const int key = j0 + ps * K_RPP + ld_row;
-            kreg[ps] = key < Lk
-                ? *reinterpret_cast<const u32x4 *>(Kp + (size_t)key * D + ld_ch * 8) : zero4;
+        for (int i = 0; i < K_PER_T; ++i) {
+            const int ci = tid + i * kThreads;
+            const int key = tk * kBN + ci / CPR;
+            const bool ok = ci < K_CHUNKS && tk < n && key < Lk;
+            stg_k[i] = ok ? *reinterpret_cast<const u32x4 *>(Kp + (size_t)key * D + (ci % CPR) * 8)
+                          : zero4;
         }
 #pragma unroll
         for (int e = 0; e < KG; ++e) {
-            const int key = j0 + ld_row * KG + e;
-            vreg[e] = key < Lk
-                ? *reinterpret_cast<const u32x4 *>(Vp + (size_t)key * D + ld_ch * 8) : zero4;
+            const int key = tv * kBN + v_grp * KG + e;
+            const bool ok = tid < V_ITEMS && tv < n && key < Lk;
+            stg_v[e] = ok ? *reinterpret_cast<const u32x4 *>(Vp + (size_t)key * D + v_ch * 8)
+                          : zero4;
         }
     };
 
-    auto swrite = [&](int buf) {
-        uint16_t *kt = lds + buf * STAGE;
-        uint16_t *vt = kt + KTILE;
+    auto swrite = [&](int tk, int tv) {
+        if (tk < n) {
+            uint16_t *kt = lds + (tk & 1) * KTILE;
 #pragma unroll
-        for (int ps = 0; ps < K_PASSES; ++ps)
-            *reinterpret_cast<u32x4 *>(kt + (ps * K_RPP + ld_row) * KSTR + ld_ch * 8) = kreg[ps];
-        const int pos = vt_pos(ld_row * KG);
+            for (int i = 0; i < K_PER_T; ++i) {
+                const int ci = tid + i * kThreads;
+                if (ci < K_CHUNKS) {
+                    const int row = ci / CPR;
+                    const int c = (ci % CPR) ^ k_swz<D>(row);
+                    *reinterpret_cast<u32x4 *>(kt + row * D + c * 8) = stg_k[i];
+                }
+            }
+        }
+        if (tv >= 0 && tv < n && tid < V_ITEMS) {
+            uint16_t *vt = lds + 2 * KTILE + (tv & 1) * VTILE;
+            const int pos = vt_pos(v_grp * KG);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint16_t *dst = vt + (ld_ch * 8 + e) * VSTR + pos;
-            if constexpr (KG == 4) {
-                u32x2 w = {half_of(vreg[0], e) | (half_of(vreg[1], e) << 16),
-                           half_of(vreg[2], e) | (half_of(vreg[3], e) << 16)};
-                *reinterpret_cast<u32x2 *>(dst) = w;
-            } else if constexpr (KG == 2) {
-                *reinterpret_cast<uint32_t *>(dst) = half_of(vreg[0], e) | (half_of(vreg[1], e) << 16);
-            } else {
-                *dst = (uint16_t)half_of(vreg[0], e);
+            for (int e = 0; e < 8; ++e) {
+                uint16_t *dst = vt + (v_ch * 8 + e) * VSTR + pos;
+                if constexpr (KG == 4) {
+                    u32x2 w = {half_of(stg_v[0], e) | (half_of(stg_v[1], e) << 16),
+                               half_of(stg_v[2], e) | (half_of(stg_v[3], e) << 16)};
+                    *reinterpret_cast<u32x2 *>(dst) = w;
+                } else if constexpr (KG == 2) {
+                    *reinterpret_cast<uint32_t *>(dst) =
+                        half_of(stg_v[0], e) | (half_of(stg_v[1], e) << 16);
+                } else {
+                    *dst = (uint16_t)half_of(stg_v[0], e);
+                }
             }
         }
     };
 
+    // ---- per-wave state
     f32x16 oacc[DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float m_run = -INFINITY;  // running max of scale*log2(e)*score
+    f32x16 s[KB];
+    u32x4 pf[KB][2];
+    float m_run = -INFINITY;  // running max of scale*log2(e)*score (possibly stale by < kLazy)
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
 
-    if (n_tiles > 0) {
-        gload(0);
-        swrite(0);
-        __syncthreads();
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < n_tiles) gload(t + 1);
-        const int j0 = t * kBN;
-        const bool wave_active = !CAUSAL || (j0 <= qw0 + kQRows - 1);
-        if (wave_active) {
-            const uint16_t *kt = lds + cur * STAGE;
-            const uint16_t *vt = kt + KTILE;
-
-            // S^T block kb: lane (query l32, group g), register r holds key
-            // j0 + 32*kb + 8*(r/4) + 4*g + r%4.
-            f32x16 s[KB];
+    auto qk = [&](int j) {
+        const uint16_t *kt = lds + (j & 1) * KTILE;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            const int row = kb * 32 + l32;
+            const int swz = k_swz<D>(row);
 #pragma unroll
-                for (int kk = 0; kk < DK; ++kk) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        kt + (kb * 32 + l32) * KSTR + kk * 16 + g * 8);
-                    s[kb] = mfma32<BF16>(a, qf[kk], s[kb]);
-                }
+            for (int kk = 0; kk < DK; ++kk) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                    kt + row * D + (((2 * kk + g) ^ swz) * 8));
+                s[kb] = mfma32<BF16>(a, qf[kk], s[kb]);
             }
+        }
+    };
 
-            const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
-            if (need_mask) {
+    auto pv = [&](int j) {
+        const uint16_t *vt = lds + 2 * KTILE + (j & 1) * VTILE;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+        for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool ok = key < Lk && (!CAUSAL || key <= my_q);
-                        s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                    }
+            for (int kc = 0; kc < 2 * KB; ++kc) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                    vt + (cb * 32 + l32) * VSTR + kc * 16 + g * 8);
+                oacc[cb] = mfma32<BF16>(a, pf[kc >> 1][kc & 1], oacc[cb]);
             }
-            float mx = -INFINITY;
+    };
+
+    auto softmax = [&](int j) {
+        const int j0 = j * kBN;
+        const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
-            const float m_new = fmaxf(m_run, m_tile);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    const bool ok = key < Lk && (!CAUSAL || key <= my_q);
+                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+        mx = fmaxf(mx, other_half(mx));
+        const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+        const bool grow = m_tile > m_run + kLazy;
+        if (__any(grow)) {
+            const float m_new = grow ? m_tile : m_run;
+            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-
-            // P = exp2(c*s - m), packed to 16 bits as the P.V B operand.
-            u32x4 pf[KB][2];
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float s0 = s[kb][ch * 8 + 2 * w];
-                        const float s1 = s[kb][ch * 8 + 2 * w + 1];
-                        float p0 = fast_exp2(__builtin_fmaf(s0, c, -m_use));
-                        float p1 = fast_exp2(__builtin_fmaf(s1, c, -m_use));
-                        if (need_mask) {
-                            p0 = (s0 == -INFINITY) ? 0.f : p0;
-                            p1 = (s1 == -INFINITY) ? 0.f : p1;
-                        }
-                        lsum += p0 + p1;
-                        pf[kb][ch][w] = pack2<BF16>(p0, p1);
-                    }
-            l_run += lsum;
-
-            // O^T block cb += V^T[cb rows][keys] . P^T[keys][queries]
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch) {
-                        const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                            vt + (cb * 32 + l32) * VSTR + (kb * 2 + ch) * 16 + g * 8);
-                        oacc[cb] = mfma32<BF16>(a, pf[kb][ch], oacc[cb]);
-                    }
         }
-        if (t + 1 < n_tiles) swrite(cur ^ 1);
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float s0 = s[kb][ch * 8 + 2 * w];
+                    const float s1 = s[kb][ch * 8 + 2 * w + 1];
+                    float p0 = fast_exp2(__builtin_fmaf(s0, c, -m_use));
+                    float p1 = fast_exp2(__builtin_fmaf(s1, c, -m_use));
+                    if (need_mask) {
+                        p0 = (s0 == -INFINITY) ? 0.f : p0;
+                        p1 = (s1 == -INFINITY) ? 0.f : p1;
+                    }
+                    lsum += p0 + p1;
+                    pf[kb][ch][w] = pack2<BF16>(p0, p1);
+                }
+        l_run += lsum;
+    };
+
+    // ---- prologue: K tile 0 in LDS, K tile 1 and V tile 0 in flight
+    if (n > 0) {
+        gload(0, n);
+        swrite(0, -1);
+        gload(1, 0);
+    }
+    __syncthreads();
+
+    // ---- phases: group g issues MFMA work for pair j in phase 2j+g and the
+    // softmax of tile j in phase 2j+g+1.  K tile j is read in phases 2j and
+    // 2j+1, V tile j in 2j+2 and 2j+3; both rings hold two tiles, refilled
+    // in phase 2j+1 (K tile j+1, V tile j).
+    const int n_phases = n > 0 ? 2 * n + 2 : 0;
+    for (int ph = 0; ph < n_phases; ++ph) {
+        const int t = ph - grp;
+        if (t >= 0) {
+            const int j = t >> 1;
+            if ((t & 1) == 0) {
+                __builtin_amdgcn_s_setprio(1);
+                if (j >= 1 && j - 1 < n_w) pv(j - 1);
+                if (j < n_w) qk(j);
+                __builtin_amdgcn_s_setprio(0);
+            } else if (j < n_w) {
+                softmax(j);
+            }
+        }
+        if (ph & 1) {
+            const int j = ph >> 1;
+            swrite(j + 1, j);
+            gload(j + 2, j + 1);
+        }
         __syncthreads();
     }
 
-    // Epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l).
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l)
+    const float l_tot = l_run + other_half(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (q_ok) {
         uint16_t *orow = p.O + base + (size_t)my_q * D;
