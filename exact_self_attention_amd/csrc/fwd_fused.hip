@@ -20,25 +20,27 @@
 //    current one) while the other runs the softmax of its current tile on
 //    the vector ALU, so each SIMD keeps its matrix core and its VALU busy at
 //    the same time.
+//  * K and V tiles go from device memory straight into LDS (buffer loads
+//    with the LDS bit: no staging registers; rows past the valid key length
+//    fall outside the buffer range and read as zero, so they are never read
+//    from memory).  Both rings hold two tiles in separate LDS arrays; a tile
+//    is fetched two phases before its first use.
+//  * Both tiles are row-major with their 16-byte chunks XOR-swizzled by row
+//    so that the 128-bit K fragment reads and the transposing V reads
+//    (ds_read_b64_tr_b16) are free of bank conflicts.
 //  * S^T (keys as MFMA rows, queries as columns) keeps one query's scores in
 //    one lane: a row max or sum is in-lane work plus one exchange with the
-//    lane 32 away (v_permlane32_swap).
-//  * The S^T accumulator layout (lane = query + 32*g, register r = key
-//    8*(r/4) + 4*g + r%4) is used as the B operand of the P.V MFMA as it
-//    is.  V is stored transposed in LDS with keys permuted inside each group
-//    of 16 so that lane group g reads its 8 keys with one 128-bit load.
-//  * K is stored row-major with 16-byte chunks XOR-swizzled by row, so the
-//    128-bit fragment reads of 8 or 16 consecutive rows hit distinct banks.
-//  * Q stays in VGPRs.  Global loads of the tiles two phases ahead are in
-//    flight while the current ones are used (register staging, then LDS).
-//  * exp2 with scale*log2(e) folded into one FMA; the running max is only
-//    raised when a tile's max exceeds it by more than 2^8 (lazy rescale):
-//    the result is the same, probabilities stay below 256.
+//    lane 32 away (v_permlane32_swap).  The S^T accumulator layout (lane =
+//    query + 32*g, register r = key 8*(r/4) + 4*g + r%4) is the B operand of
+//    the P.V MFMA as it is; the transposing reads deliver V^T in the same key
+//    order.
+//  * Q stays in VGPRs.  exp2 with scale*log2(e) folded into one FMA; the
+//    running max is raised only when a tile's max exceeds it by more than
+//    2^8 (lazy rescale): the result is the same, probabilities stay < 256.
 //  * Causal and key-padding masks: the loop stops at the last key tile any
 //    row of the workgroup can see, each wave skips tiles wholly after its
-//    rows, per-element masking only on tiles that straddle a boundary, and
-//    key rows past the valid length are never read.  Causal grids launch
-//    the heaviest query tiles first.
+//    rows, and per-element masking runs only on tiles that straddle a
+//    boundary.  Causal grids launch the heaviest query tiles first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,6 +58,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -64,6 +69,8 @@ constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.0f;            // log2 of the largest unscaled probability
+// Buffer resource word 3 for raw (untyped) 32-bit loads on gfx9-class parts.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -92,51 +99,48 @@ __device__ __forceinline__ float other_half(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     // r[0] holds the low half of the wave twice, r[1] the high half twice.
-    const uint32_t lo = r[0], hi = r[1];
-    return __builtin_bit_cast(float, (__lane_id() < 32) ? hi : lo);
+    return __builtin_bit_cast(float, (__lane_id() < 32) ? (uint32_t)r[1] : (uint32_t)r[0]);
 }
 
-// Position of key k (0..kBN-1) inside a transposed V tile row.  Within each
-// group of 16 keys the order is 0-3, 8-11, 4-7, 12-15, so that the 8 keys a
-// lane group holds in the S^T accumulator (4g..4g+3 and 8+4g..8+4g+3) are
-// contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-    const int kk = k & 15;
-    return (k & ~15) | (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
-__device__ __forceinline__ uint32_t half_of(u32x4 v, int e) {
-    const uint32_t w = v[e >> 1];
-    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// XOR swizzle of the 16-byte chunk index of K tile row `row` (D halves per
-// row): rows that share a 256-byte bank window get distinct chunk offsets.
+// XOR swizzle of the 16-byte chunk index within row `row` of a tile with D
+// halves per row.  It makes (a) the 128-bit fragment reads of 16
+// consecutive rows at one logical chunk and (b) the transposing 8-byte reads
+// of 4 consecutive rows x 4 consecutive chunks land in distinct bank groups.
 template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    constexpr int RP = 128 / D;  // rows per 256 bytes
-    constexpr int CPR = D / 8;   // chunks per row
-    return (row / RP) % CPR;
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else return (row >> 2) & 3;
+}
+
+// Workgroup barrier without the memory-model waits of __syncthreads: the
+// code orders its LDS traffic itself (fragment reads are consumed before the
+// barrier; tile loads are waited for explicitly).
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_tile_loads() {
+    // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int D, bool BF16, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
-    constexpr int KTILE = kBN * D;                // halves per K tile (no padding)
-    constexpr int VSTR = kBN + 8;                 // LDS row stride of a V^T tile
-    constexpr int VTILE = D * VSTR;
-    constexpr int K_CHUNKS = kBN * CPR;
-    constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
-    constexpr int KG_RAW = kBN * D / (8 * kThreads);
-    constexpr int KG = KG_RAW >= 1 ? KG_RAW : 1;  // keys per thread in a V tile load
-    constexpr int V_ITEMS = (kBN / KG) * CPR;
+    constexpr int TILE = kBN * D;                 // halves per K or V tile
+    constexpr int TILE_INSTR = kBN * CPR / 64;    // 1 KB load instructions per tile
+    constexpr int INSTR_PER_WAVE = (TILE_INSTR + kWaves - 1) / kWaves;
     constexpr int KB = kBN / 32;                  // 32-key blocks per tile
     constexpr int DK = D / 16;                    // 16-deep k-steps of Q.K
     constexpr int DB = D / 32;                    // 32-wide column blocks of O
-    static_assert(KG == 1 || KG == 2 || KG == 4, "V tile load shape");
-    static_assert(V_ITEMS <= kThreads, "V tile load shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * KTILE + 2 * VTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -180,61 +184,32 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     for (int kk = 0; kk < DK; ++kk)
         qf[kk] = q_ok ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + kk * 16 + g * 8)
                       : zero4;
+    wait_tile_loads();
 
-    // ---- tile loads: global -> staging registers -> LDS
-    u32x4 stg_k[K_PER_T];
-    u32x4 stg_v[KG];
-    const int v_ch = tid % CPR;
-    const int v_grp = tid / CPR;
-
-    auto gload = [&](int tk, int tv) {
+    // ---- tile loads, device memory -> LDS.  Load instruction t of a tile
+    // fills LDS bytes [1024 t, 1024 t + 1024); lane i writes 16 bytes at
+    // 1024 t + 16 i, i.e. physical chunk P = 64 t + i = row * CPR + chunk'.
+    // The lane therefore fetches logical chunk chunk' ^ swz(row).
+    uint32_t voff[INSTR_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int ci = tid + i * kThreads;
-            const int key = tk * kBN + ci / CPR;
-            const bool ok = ci < K_CHUNKS && tk < n && key < Lk;
-            stg_k[i] = ok ? *reinterpret_cast<const u32x4 *>(Kp + (size_t)key * D + (ci % CPR) * 8)
-                          : zero4;
-        }
+    for (int i = 0; i < INSTR_PER_WAVE; ++i) {
+        const int t = wave + i * kWaves;
+        const int P = 64 * t + lane;
+        const int row = P / CPR;
+        const int c = (P % CPR) ^ swz<D>(row);
+        voff[i] = (uint32_t)(row * D * 2 + c * 16);
+    }
+    auto load_tile = [&](const uint16_t *src, uint16_t *dst, int j) {
+        const int j0 = j * kBN;
+        const int rows = min(kBN, Lk - j0);
+        __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(src + (size_t)j0 * D), 0, rows * D * 2, kBufferWord3);
 #pragma unroll
-        for (int e = 0; e < KG; ++e) {
-            const int key = tv * kBN + v_grp * KG + e;
-            const bool ok = tid < V_ITEMS && tv < n && key < Lk;
-            stg_v[e] = ok ? *reinterpret_cast<const u32x4 *>(Vp + (size_t)key * D + v_ch * 8)
-                          : zero4;
-        }
-    };
-
-    auto swrite = [&](int tk, int tv) {
-        if (tk < n) {
-            uint16_t *kt = lds + (tk & 1) * KTILE;
-#pragma unroll
-            for (int i = 0; i < K_PER_T; ++i) {
-                const int ci = tid + i * kThreads;
-                if (ci < K_CHUNKS) {
-                    const int row = ci / CPR;
-                    const int c = (ci % CPR) ^ k_swz<D>(row);
-                    *reinterpret_cast<u32x4 *>(kt + row * D + c * 8) = stg_k[i];
-                }
-            }
-        }
-        if (tv >= 0 && tv < n && tid < V_ITEMS) {
-            uint16_t *vt = lds + 2 * KTILE + (tv & 1) * VTILE;
-            const int pos = vt_pos(v_grp * KG);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint16_t *dst = vt + (v_ch * 8 + e) * VSTR + pos;
-                if constexpr (KG == 4) {
-                    u32x2 w = {half_of(stg_v[0], e) | (half_of(stg_v[1], e) << 16),
-                               half_of(stg_v[2], e) | (half_of(stg_v[3], e) << 16)};
-                    *reinterpret_cast<u32x2 *>(dst) = w;
-                } else if constexpr (KG == 2) {
-                    *reinterpret_cast<uint32_t *>(dst) =
-                        half_of(stg_v[0], e) | (half_of(stg_v[1], e) << 16);
-                } else {
-                    *dst = (uint16_t)half_of(stg_v[0], e);
-                }
-            }
+        for (int i = 0; i < INSTR_PER_WAVE; ++i) {
+            const int t = wave + i * kWaves;
+            if (t < TILE_INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (lds_void *)(dst + t * 512), 16, voff[i], 0, 0, 0);
         }
     };
 
@@ -250,33 +225,66 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
 
-    auto qk = [&](int j) {
-        const uint16_t *kt = lds + (j & 1) * KTILE;
+    // K fragment (A operand of S^T): key row kb*32 + l32, dims 16 kk + 8 g .. +7
+    int k_off[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) k_off[kb] = (kb * 32 + l32) * D;
+    auto qk = [&](const uint16_t *kt) {
+        u32x4 a[KB][DK];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            const int sw = swz<D>(row);
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk)
+                a[kb][kk] = *reinterpret_cast<const u32x4 *>(kt + k_off[kb] + (((2 * kk + g) ^ sw) * 8));
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            const int row = kb * 32 + l32;
-            const int swz = k_swz<D>(row);
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                    kt + row * D + (((2 * kk + g) ^ swz) * 8));
-                s[kb] = mfma32<BF16>(a, qf[kk], s[kb]);
-            }
+            for (int kk = 0; kk < DK; ++kk) s[kb] = mfma32<BF16>(a[kb][kk], qf[kk], s[kb]);
         }
     };
 
-    auto pv = [&](int j) {
-        const uint16_t *vt = lds + 2 * KTILE + (j & 1) * VTILE;
+    // V^T fragment (A operand of P.V) for column block cb, 16-key chunk kc:
+    // two transposing reads, rows 16 kc + 8 h + 4 g + (lane%16)/4, logical
+    // chunk 4 cb + 2 ((lane/16)%2) + (lane%4)/2, 8-byte half lane%2; they
+    // return V[16kc + 8h + 4g + t][32 cb + l32] for t = 0..3.
+    int v_off[2][2];  // [kc & 1][h] byte-free half offsets within a 32-key half tile
+    {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
+                v_off[kc][h] = row * D;
+            }
+    }
+    auto pv = [&](const uint16_t *vt) {
+        u32x4 a[DB][2 * KB];
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
             for (int kc = 0; kc < 2 * KB; ++kc) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                    vt + (cb * 32 + l32) * VSTR + kc * 16 + g * 8);
-                oacc[cb] = mfma32<BF16>(a, pf[kc >> 1][kc & 1], oacc[cb]);
+                i16x4 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
+                    const int chunk = (4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ swz<D>(row);
+                    const uint16_t *src = vt + (kc >> 1) * 32 * D + v_off[kc & 1][h] + chunk * 8 + (lane & 1) * 4;
+                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)src);
+                }
+                const u32x2 lo = __builtin_bit_cast(u32x2, part[0]);
+                const u32x2 hi = __builtin_bit_cast(u32x2, part[1]);
+                a[cb][kc] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
             }
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+            for (int kc = 0; kc < 2 * KB; ++kc)
+                oacc[cb] = mfma32<BF16>(a[cb][kc], pf[kc >> 1][kc & 1], oacc[cb]);
     };
 
     auto softmax = [&](int j) {
@@ -332,38 +340,51 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         l_run += lsum;
     };
 
-    // ---- prologue: K tile 0 in LDS, K tile 1 and V tile 0 in flight
-    if (n > 0) {
-        gload(0, n);
-        swrite(0, -1);
-        gload(1, 0);
-    }
-    __syncthreads();
-
-    // ---- phases: group g issues MFMA work for pair j in phase 2j+g and the
-    // softmax of tile j in phase 2j+g+1.  K tile j is read in phases 2j and
-    // 2j+1, V tile j in 2j+2 and 2j+3; both rings hold two tiles, refilled
-    // in phase 2j+1 (K tile j+1, V tile j).
-    const int n_phases = n > 0 ? 2 * n + 2 : 0;
-    for (int ph = 0; ph < n_phases; ++ph) {
+    // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
+    // and the softmax of tile j in phase 2j+1; group B runs one phase later.
+    // K tile j is read in phases 2j and 2j+1, V tile j in 2j+2 and 2j+3.
+    // Tile loads for K j+1 and V j start at phase 2j and are waited for at
+    // the end of phase 2j+1.  Slot arrays are passed in statically so the
+    // compiler can tell the in-flight loads from the tiles being read.
+    auto phase = [&](int ph, const uint16_t *k_cur, const uint16_t *v_prev,
+                     uint16_t *k_next, uint16_t *v_cur) {
+        const int j = ph >> 1;
+        if ((ph & 1) == 0) {
+            if (j + 1 < n) load_tile(Kp, k_next, j + 1);
+            if (j < n) load_tile(Vp, v_cur, j);
+        }
         const int t = ph - grp;
         if (t >= 0) {
-            const int j = t >> 1;
+            const int jj = t >> 1;
             if ((t & 1) == 0) {
                 __builtin_amdgcn_s_setprio(1);
-                if (j >= 1 && j - 1 < n_w) pv(j - 1);
-                if (j < n_w) qk(j);
+                if (jj >= 1 && jj - 1 < n_w) pv(v_prev);
+                if (jj < n_w) qk(k_cur);
                 __builtin_amdgcn_s_setprio(0);
-            } else if (j < n_w) {
-                softmax(j);
+            } else if (jj < n_w) {
+                softmax(jj);
             }
         }
-        if (ph & 1) {
-            const int j = ph >> 1;
-            swrite(j + 1, j);
-            gload(j + 2, j + 1);
-        }
-        __syncthreads();
+        if (ph & 1) wait_tile_loads();
+        barrier();
+    };
+
+    // prologue: K tile 0
+    if (n > 0) {
+        load_tile(Kp, sK0, 0);
+        wait_tile_loads();
+    }
+    barrier();
+
+    // Phases 4i .. 4i+3 handle tiles j = 2i (slots 0) and j = 2i+1 (slots 1).
+    // For group B the "current" tile of an odd phase 2j+1 is tile j as well,
+    // so the slot arguments depend only on the phase.
+    const int n_phases = n > 0 ? 2 * n + 2 : 0;
+    for (int ph = 0; ph < n_phases; ph += 4) {
+        phase(ph + 0, sK0, sV1, sK1, sV0);
+        if (ph + 1 < n_phases) phase(ph + 1, sK0, sV1, sK1, sV0);
+        if (ph + 2 < n_phases) phase(ph + 2, sK1, sV0, sK0, sV1);
+        if (ph + 3 < n_phases) phase(ph + 3, sK1, sV0, sK0, sV1);
     }
 
     // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l)
