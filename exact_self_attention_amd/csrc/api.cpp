@@ -104,7 +104,11 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void *Q, const void *K, const v
     p.BH = (int)(B * H);
     p.H = (int)H;
     p.n_qtiles = 0;
+    // The kernel needs a positive exp2 scale (masked scores are -inf and must
+    // map to exactly 0).  A zero scale becomes 1e-30: every score times it
+    // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
     const hipError_t e = attn::launch_fwd(dtype == ATTN_BF16, (int)d, causal != 0, p,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

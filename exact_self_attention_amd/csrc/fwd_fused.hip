@@ -225,68 +225,101 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
 
-    // K fragment (A operand of S^T): key row kb*32 + l32, dims 16 kk + 8 g .. +7
-    int k_off[KB];
+    // K fragment (A operand of S^T) for 32-key block kb, k-step kk: key row
+    // kb*32 + l32, dims 16 kk + 8 g .. +7, one 128-bit read.
+    auto frag_k = [&](const uint16_t *kt, int kb, int kk) -> u32x4 {
+        const int row = kb * 32 + l32;
+        return *reinterpret_cast<const u32x4 *>(kt + row * D + (((2 * kk + g) ^ swz<D>(row)) * 8));
+    };
+    // V^T fragment (A operand of P.V) for column block cb, 16-key chunk kc:
+    // two transposing reads at rows 16 kc + 8 h + 4 g + (lane%16)/4, logical
+    // chunk 4 cb + 2 ((lane/16)%2) + (lane%4)/2, 8-byte half lane%2; they
+    // return V[16kc + 8h + 4g + t][32 cb + l32] for t = 0..3, the key order
+    // of the P registers.
+    auto frag_v = [&](const uint16_t *vt, int cb, int kc) -> u32x4 {
+        i16x4 part[2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) k_off[kb] = (kb * 32 + l32) * D;
-    auto qk = [&](const uint16_t *kt) {
-        u32x4 a[KB][DK];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int row = kb * 32 + l32;
-            const int sw = swz<D>(row);
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk)
-                a[kb][kk] = *reinterpret_cast<const u32x4 *>(kt + k_off[kb] + (((2 * kk + g) ^ sw) * 8));
+        for (int h = 0; h < 2; ++h) {
+            const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
+            const int chunk = (4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ swz<D>(row);
+            part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(vt + row * D + chunk * 8 + (lane & 1) * 4));
         }
+        const u32x2 lo = __builtin_bit_cast(u32x2, part[0]);
+        const u32x2 hi = __builtin_bit_cast(u32x2, part[1]);
+        return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    };
+
+    // MFMA work of one phase as a list of steps of up to 4 MFMAs: first the
+    // P.V steps (one per 32-column block of O, over the 4 key chunks), then
+    // the Q.K steps (per 32-key block, 4 k-steps each).  Fragments of step
+    // s+1 are read from LDS before the MFMAs of step s are issued, so LDS
+    // latency hides behind matrix-core work.
+    constexpr int QK_PER = DK < 4 ? DK : 4;            // MFMAs per Q.K step
+    constexpr int QK_STEPS_PER_KB = DK / QK_PER;
+    constexpr int PV_STEPS = DB;
+    constexpr int QK_STEPS = KB * QK_STEPS_PER_KB;
+    auto load_step = [&](int st, const uint16_t *kt, const uint16_t *vt, bool do_pv, u32x4 *f) {
+        if (st < PV_STEPS) {
+            if (do_pv) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+                for (int kc = 0; kc < 4; ++kc) f[kc] = frag_v(vt, st, kc);
+            }
+        } else {
+            const int q = st - PV_STEPS;
+            const int kb = q / QK_STEPS_PER_KB;
+            const int k0 = (q % QK_STEPS_PER_KB) * QK_PER;
+#pragma unroll
+            for (int i = 0; i < QK_PER; ++i) f[i] = frag_k(kt, kb, k0 + i);
+        }
+    };
+    auto mfma_step = [&](int st, bool do_pv, const u32x4 *f) {
+        if (st < PV_STEPS) {
+            if (do_pv) {
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    oacc[st] = mfma32<BF16>(f[kc], pf[kc >> 1][kc & 1], oacc[st]);
+            }
+        } else {
+            const int q = st - PV_STEPS;
+            const int kb = q / QK_STEPS_PER_KB;
+            const int k0 = (q % QK_STEPS_PER_KB) * QK_PER;
+#pragma unroll
+            for (int i = 0; i < QK_PER; ++i) s[kb] = mfma32<BF16>(f[i], qf[k0 + i], s[kb]);
+        }
+    };
+    auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, bool do_pv) {
+        constexpr int NST = PV_STEPS + QK_STEPS;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        u32x4 f[2][4];
+        if (do_pv) load_step(0, kt, vt, true, f[0]);
+        else load_step(PV_STEPS, kt, vt, false, f[PV_STEPS & 1]);
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) s[kb] = mfma32<BF16>(a[kb][kk], qf[kk], s[kb]);
+        for (int st = 0; st < NST; ++st) {
+            if (st + 1 < NST) load_step(st + 1, kt, vt, do_pv, f[(st + 1) & 1]);
+            mfma_step(st, do_pv, f[st & 1]);
         }
     };
 
-    // V^T fragment (A operand of P.V) for column block cb, 16-key chunk kc:
-    // two transposing reads, rows 16 kc + 8 h + 4 g + (lane%16)/4, logical
-    // chunk 4 cb + 2 ((lane/16)%2) + (lane%4)/2, 8-byte half lane%2; they
-    // return V[16kc + 8h + 4g + t][32 cb + l32] for t = 0..3.
-    int v_off[2][2];  // [kc & 1][h] byte-free half offsets within a 32-key half tile
-    {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
-                v_off[kc][h] = row * D;
-            }
-    }
-    auto pv = [&](const uint16_t *vt) {
-        u32x4 a[DB][2 * KB];
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-            for (int kc = 0; kc < 2 * KB; ++kc) {
-                i16x4 part[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
-                    const int chunk = (4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ swz<D>(row);
-                    const uint16_t *src = vt + (kc >> 1) * 32 * D + v_off[kc & 1][h] + chunk * 8 + (lane & 1) * 4;
-                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)src);
-                }
-                const u32x2 lo = __builtin_bit_cast(u32x2, part[0]);
-                const u32x2 hi = __builtin_bit_cast(u32x2, part[1]);
-                a[cb][kc] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-            }
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-            for (int kc = 0; kc < 2 * KB; ++kc)
-                oacc[cb] = mfma32<BF16>(a[cb][kc], pf[kc >> 1][kc & 1], oacc[cb]);
+    auto max3 = [](float a, float b, float c3) -> float {
+        float d;
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c3));
+        return d;
+    };
+    // acc + lo + hi of a packed fp16 pair (v_dot2 against (1, 1))
+    auto dot2_ones = [](uint32_t pk, float acc) -> float {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                      __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
     };
 
+    // Online softmax of tile j.  Masked scores become -inf; since c > 0 their
+    // exp2 is exactly 0.  For fp16 the normaliser sums the rounded
+    // probabilities that the P.V product uses (v_dot2, relative rounding at
+    // most 2^-11 each); bf16 rounding is too coarse for that, so bf16 sums the
+    // fp32 values.
     auto softmax = [&](int j) {
         const int j0 = j * kBN;
         const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
@@ -300,13 +333,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                     s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        float mx = max3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-        mx = fmaxf(mx, other_half(mx));
-        const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+        for (int i = 3; i + 1 < 16 * KB; i += 2)
+            mx = max3(mx, s[i / 16][i % 16], s[(i + 1) / 16][(i + 1) % 16]);
+        if constexpr ((16 * KB) % 2 == 0) mx = max3(mx, s[KB - 1][15], s[KB - 1][15]);
+        mx = max3(mx, other_half(mx), mx);
+        const float m_tile = mx * c;  // -inf stays -inf (c > 0)
         const bool grow = m_tile > m_run + kLazy;
         if (__any(grow)) {
             const float m_new = grow ? m_tile : m_run;
@@ -318,26 +351,29 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
         }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float lsum = 0.f;
+        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+        float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const float s0 = s[kb][ch * 8 + 2 * w];
-                    const float s1 = s[kb][ch * 8 + 2 * w + 1];
-                    float p0 = fast_exp2(__builtin_fmaf(s0, c, -m_use));
-                    float p1 = fast_exp2(__builtin_fmaf(s1, c, -m_use));
-                    if (need_mask) {
-                        p0 = (s0 == -INFINITY) ? 0.f : p0;
-                        p1 = (s1 == -INFINITY) ? 0.f : p1;
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w], c, neg_m));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w + 1], c, neg_m));
+                    const uint32_t pk = pack2<BF16>(p0, p1);
+                    pf[kb][ch][w] = pk;
+                    if constexpr (BF16) {
+                        // bf16 keeps 8 mantissa bits: sum the fp32 values
+                        lsum0 += p0;
+                        lsum1 += p1;
+                    } else if (w & 1) {
+                        lsum1 = dot2_ones(pk, lsum1);
+                    } else {
+                        lsum0 = dot2_ones(pk, lsum0);
                     }
-                    lsum += p0 + p1;
-                    pf[kb][ch][w] = pack2<BF16>(p0, p1);
                 }
-        l_run += lsum;
+        l_run += lsum0 + lsum1;
     };
 
     // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
@@ -357,9 +393,19 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         if (t >= 0) {
             const int jj = t >> 1;
             if ((t & 1) == 0) {
+                const bool do_pv = jj >= 1 && jj - 1 < n_w;
+                const bool do_qk = jj < n_w;
                 __builtin_amdgcn_s_setprio(1);
-                if (jj >= 1 && jj - 1 < n_w) pv(v_prev);
-                if (jj < n_w) qk(k_cur);
+                if (do_qk) {
+                    mfma_phase(k_cur, v_prev, do_pv);
+                } else if (do_pv) {
+                    u32x4 f[4];
+#pragma unroll
+                    for (int st = 0; st < PV_STEPS; ++st) {
+                        load_step(st, k_cur, v_prev, true, f);
+                        mfma_step(st, true, f);
+                    }
+                }
                 __builtin_amdgcn_s_setprio(0);
             } else if (jj < n_w) {
                 softmax(jj);

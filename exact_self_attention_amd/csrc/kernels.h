@@ -19,7 +19,7 @@ struct FwdParams {
     int BH;                     // B * H
     int H;
     int n_qtiles;               // ceil(N / query rows per workgroup)
-    float scale_log2;           // scale * log2(e)
+    float scale_log2;           // scale * log2(e), > 0
 };
 
 // Query rows each fused workgroup owns (the query tile height).
