@@ -69,6 +69,7 @@ constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.0f;            // log2 of the largest unscaled probability
+constexpr int kLoadWaves = 8;            // waves that issue tile loads (8: all, 4: group B)
 // Buffer resource word 3 for raw (untyped) 32-bit loads on gfx9-class parts.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -94,12 +95,16 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of x in the lane 32 away (lanes l and l^32 swap).
-__device__ __forceinline__ float other_half(float x) {
+// The values of x in lanes l % 32 and l % 32 + 32, for every lane l:
+// v_permlane32_swap of x with itself leaves the low half of the wave in
+// both halves of the first result and the high half in the second.
+struct Halves {
+    float lo, hi;
+};
+__device__ __forceinline__ Halves both_halves(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    // r[0] holds the low half of the wave twice, r[1] the high half twice.
-    return __builtin_bit_cast(float, (__lane_id() < 32) ? (uint32_t)r[1] : (uint32_t)r[0]);
+    return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
 }
 
 // XOR swizzle of the 16-byte chunk index within row `row` of a tile with D
@@ -123,8 +128,30 @@ __device__ __forceinline__ void barrier() {
 }
 
 __device__ __forceinline__ void wait_tile_loads() {
-    // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (gfx9 layout) over nbytes bytes at base, stride 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t nbytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+    r[3] = kBufferWord3;
+    return r;
+}
+
+// One wave-wide tile load: lane i copies the 16 bytes at byte offset voff of
+// the buffer into LDS at lds_addr + 16 i; bytes past the buffer range read
+// as zero.  Written as inline assembly so that the compiler does not add
+// waits for these loads before unrelated LDS reads: the kernel waits for
+// them itself (wait_tile_loads) before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 template <int D, bool BF16, bool CAUSAL>
@@ -132,7 +159,6 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int TILE = kBN * D;                 // halves per K or V tile
     constexpr int TILE_INSTR = kBN * CPR / 64;    // 1 KB load instructions per tile
-    constexpr int INSTR_PER_WAVE = (TILE_INSTR + kWaves - 1) / kWaves;
     constexpr int KB = kBN / 32;                  // 32-key blocks per tile
     constexpr int DK = D / 16;                    // 16-deep k-steps of Q.K
     constexpr int DB = D / 32;                    // 32-wide column blocks of O
@@ -184,32 +210,47 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     for (int kk = 0; kk < DK; ++kk)
         qf[kk] = q_ok ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + kk * 16 + g * 8)
                       : zero4;
-    wait_tile_loads();
+    // Compiler-visible s_waitcnt vmcnt(0): the Q fragments are complete
+    // before the loop, so no wait for them lands inside it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // ---- tile loads, device memory -> LDS.  Load instruction t of a tile
     // fills LDS bytes [1024 t, 1024 t + 1024); lane i writes 16 bytes at
     // 1024 t + 16 i, i.e. physical chunk P = 64 t + i = row * CPR + chunk'.
     // The lane therefore fetches logical chunk chunk' ^ swz(row).
-    uint32_t voff[INSTR_PER_WAVE];
+    // kLoadWaves waves (all 8, or group B alone) issue the loads of a tile
+    // pair at the start of even phases; instruction t = w + kLoadWaves i
+    // comes from loader wave w.
+    constexpr int LW = kLoadWaves < TILE_INSTR ? kLoadWaves : TILE_INSTR;
+    constexpr int DMA_HALF = TILE_INSTR / LW;     // loads per loader wave per tile
+    constexpr int DMA_PER_PHASE = 2 * DMA_HALF;   // K tile + V tile
+    static_assert(TILE_INSTR % LW == 0, "tile load split");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int loader = kLoadWaves == kWaves ? wave_u : wave_u - (kWaves - kLoadWaves);
+    const bool is_loader = loader >= 0 && loader < LW;
+    uint32_t voff[DMA_HALF];
 #pragma unroll
-    for (int i = 0; i < INSTR_PER_WAVE; ++i) {
-        const int t = wave + i * kWaves;
+    for (int i = 0; i < DMA_HALF; ++i) {
+        const int t = (is_loader ? loader : 0) + LW * i;
         const int P = 64 * t + lane;
         const int row = P / CPR;
         const int c = (P % CPR) ^ swz<D>(row);
         voff[i] = (uint32_t)(row * D * 2 + c * 16);
     }
-    auto load_tile = [&](const uint16_t *src, uint16_t *dst, int j) {
+    auto tile_rsrc = [&](const uint16_t *src, int j) -> i32x4 {
         const int j0 = j * kBN;
         const int rows = min(kBN, Lk - j0);
-        __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(src + (size_t)j0 * D), 0, rows * D * 2, kBufferWord3);
-#pragma unroll
-        for (int i = 0; i < INSTR_PER_WAVE; ++i) {
-            const int t = wave + i * kWaves;
-            if (t < TILE_INSTR)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc, (lds_void *)(dst + t * 512), 16, voff[i], 0, 0, 0);
+        return make_rsrc(src + (size_t)j0 * D, (uint32_t)(rows * D * 2));
+    };
+    // Load k (0 <= k < DMA_PER_PHASE) of this loader wave: K tile, then V.
+    auto issue_load = [&](int k, bool ld_k, bool ld_v, const i32x4 &rk, const i32x4 &rv,
+                          uint16_t *k_dst, uint16_t *v_dst) {
+        const int i = k % DMA_HALF;
+        const uint32_t t = (uint32_t)(loader + LW * i);
+        if (k < DMA_HALF) {
+            if (ld_k) dma16(rk, (uint32_t)(uintptr_t)(lds_void *)k_dst + t * 1024u, voff[i]);
+        } else {
+            if (ld_v) dma16(rv, (uint32_t)(uintptr_t)(lds_void *)v_dst + t * 1024u, voff[i]);
         }
     };
 
@@ -288,8 +329,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
             for (int i = 0; i < QK_PER; ++i) s[kb] = mfma32<BF16>(f[i], qf[k0 + i], s[kb]);
         }
     };
+    constexpr int NST = PV_STEPS + QK_STEPS;
     auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, bool do_pv) {
-        constexpr int NST = PV_STEPS + QK_STEPS;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -309,17 +350,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c3));
         return d;
     };
-    // acc + lo + hi of a packed fp16 pair (v_dot2 against (1, 1))
-    auto dot2_ones = [](uint32_t pk, float acc) -> float {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
-                                      __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
-    };
-
     // Online softmax of tile j.  Masked scores become -inf; since c > 0 their
-    // exp2 is exactly 0.  For fp16 the normaliser sums the rounded
-    // probabilities that the P.V product uses (v_dot2, relative rounding at
-    // most 2^-11 each); bf16 rounding is too coarse for that, so bf16 sums the
-    // fp32 values.
+    // exp2 is exactly 0.  The row max and the row sum are trees (short
+    // dependency chains); the normaliser sums the fp32 probabilities.
     auto softmax = [&](int j) {
         const int j0 = j * kBN;
         const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
@@ -333,12 +366,18 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                     s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
         }
-        float mx = max3(s[0][0], s[0][1], s[0][2]);
+        static_assert(KB == 2, "the reductions below assume 32 scores per lane");
+        float t1[11];
 #pragma unroll
-        for (int i = 3; i + 1 < 16 * KB; i += 2)
-            mx = max3(mx, s[i / 16][i % 16], s[(i + 1) / 16][(i + 1) % 16]);
-        if constexpr ((16 * KB) % 2 == 0) mx = max3(mx, s[KB - 1][15], s[KB - 1][15]);
-        mx = max3(mx, other_half(mx), mx);
+        for (int i = 0; i < 10; ++i)
+            t1[i] = max3(s[(3 * i) / 16][(3 * i) % 16], s[(3 * i + 1) / 16][(3 * i + 1) % 16],
+                         s[(3 * i + 2) / 16][(3 * i + 2) % 16]);
+        t1[10] = fmaxf(s[1][14], s[1][15]);
+        const float t2a = max3(t1[0], t1[1], t1[2]), t2b = max3(t1[3], t1[4], t1[5]);
+        const float t2c = max3(t1[6], t1[7], t1[8]), t2d = fmaxf(t1[9], t1[10]);
+        float mx = max3(max3(t2a, t2b, t2c), t2d, t2d);
+        const Halves mh = both_halves(mx);
+        mx = fmaxf(mh.lo, mh.hi);
         const float m_tile = mx * c;  // -inf stays -inf (c > 0)
         const bool grow = m_tile > m_run + kLazy;
         if (__any(grow)) {
@@ -352,28 +391,23 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                 for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-        float lsum0 = 0.f, lsum1 = 0.f;
+        float pr[32];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w], c, neg_m));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w + 1], c, neg_m));
-                    const uint32_t pk = pack2<BF16>(p0, p1);
-                    pf[kb][ch][w] = pk;
-                    if constexpr (BF16) {
-                        // bf16 keeps 8 mantissa bits: sum the fp32 values
-                        lsum0 += p0;
-                        lsum1 += p1;
-                    } else if (w & 1) {
-                        lsum1 = dot2_ones(pk, lsum1);
-                    } else {
-                        lsum0 = dot2_ones(pk, lsum0);
-                    }
+                    const int i = kb * 16 + ch * 8 + 2 * w;
+                    pr[i] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w], c, neg_m));
+                    pr[i + 1] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w + 1], c, neg_m));
+                    pf[kb][ch][w] = pack2<BF16>(pr[i], pr[i + 1]);
                 }
-        l_run += lsum0 + lsum1;
+#pragma unroll
+        for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
+        l_run += pr[0];
     };
 
     // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
@@ -385,9 +419,14 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     auto phase = [&](int ph, const uint16_t *k_cur, const uint16_t *v_prev,
                      uint16_t *k_next, uint16_t *v_cur) {
         const int j = ph >> 1;
-        if ((ph & 1) == 0) {
-            if (j + 1 < n) load_tile(Kp, k_next, j + 1);
-            if (j < n) load_tile(Vp, v_cur, j);
+        // tile loads of this phase: K tile j+1 and V tile j, in even phases
+        if ((ph & 1) == 0 && is_loader) {
+            const bool ld_k = j + 1 < n;
+            const bool ld_v = j < n;
+            const i32x4 rk = tile_rsrc(Kp, ld_k ? j + 1 : 0);
+            const i32x4 rv = tile_rsrc(Vp, ld_v ? j : 0);
+#pragma unroll
+            for (int k = 0; k < DMA_PER_PHASE; ++k) issue_load(k, ld_k, ld_v, rk, rv, k_next, v_cur);
         }
         const int t = ph - grp;
         if (t >= 0) {
@@ -395,7 +434,6 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
             if ((t & 1) == 0) {
                 const bool do_pv = jj >= 1 && jj - 1 < n_w;
                 const bool do_qk = jj < n_w;
-                __builtin_amdgcn_s_setprio(1);
                 if (do_qk) {
                     mfma_phase(k_cur, v_prev, do_pv);
                 } else if (do_pv) {
@@ -406,7 +444,6 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                         mfma_step(st, true, f);
                     }
                 }
-                __builtin_amdgcn_s_setprio(0);
             } else if (jj < n_w) {
                 softmax(jj);
             }
@@ -417,7 +454,11 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
 
     // prologue: K tile 0
     if (n > 0) {
-        load_tile(Kp, sK0, 0);
+        const i32x4 rk = tile_rsrc(Kp, 0);
+        if (is_loader) {
+#pragma unroll
+            for (int k = 0; k < DMA_HALF; ++k) issue_load(k, true, false, rk, rk, sK0, sV0);
+        }
         wait_tile_loads();
     }
     barrier();
@@ -434,7 +475,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     }
 
     // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l)
-    const float l_tot = l_run + other_half(l_run);
+    const Halves lh = both_halves(l_run);
+    const float l_tot = lh.lo + lh.hi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (q_ok) {
         uint16_t *orow = p.O + base + (size_t)my_q * D;
