@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace attn {
@@ -69,7 +71,6 @@ constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.0f;            // log2 of the largest unscaled probability
-constexpr int kLoadWaves = 8;            // waves that issue tile loads (8: all, 4: group B)
 // Buffer resource word 3 for raw (untyped) 32-bit loads on gfx9-class parts.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -127,6 +128,16 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Scheduling pattern: N times (one MFMA, then R LDS reads).
+template <int N, int R>
+__device__ __forceinline__ void sched_mfma_reads() {
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS read
+        sched_mfma_reads<N - 1, R>();
+    }
+}
+
 __device__ __forceinline__ void wait_tile_loads() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -163,6 +174,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int DK = D / 16;                    // 16-deep k-steps of Q.K
     constexpr int DB = D / 32;                    // 32-wide column blocks of O
 
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ[kBM * D];
     __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
@@ -204,30 +216,39 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     if (CAUSAL) n_w = (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN;
     if (qw0 >= N) n_w = 0;
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    u32x4 qf[DK];
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // The query tile goes to LDS once (same swizzled row-major layout as the
+    // K tiles; rows past N read as zero); each wave re-reads its Q fragments
+    // there instead of holding them in 8 x DK VGPRs.
+    {
+        constexpr int QI = kBM * CPR / 64;        // 1 KB load instructions
+        static_assert(QI % kWaves == 0, "query tile load split");
+        const int rows = min(kBM, N - q0);
+        const i32x4 rq = make_rsrc(Qp + (size_t)q0 * D, (uint32_t)(rows * D * 2));
+        const uint32_t lds = (uint32_t)(uintptr_t)(lds_void *)sQ;
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-        qf[kk] = q_ok ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + kk * 16 + g * 8)
-                      : zero4;
-    // Compiler-visible s_waitcnt vmcnt(0): the Q fragments are complete
-    // before the loop, so no wait for them lands inside it.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+        for (int i = 0; i < QI / kWaves; ++i) {
+            const int t = wave + kWaves * i;
+            const int P = 64 * t + lane;
+            const int row = P / CPR;
+            const int c = (P % CPR) ^ swz<D>(row);
+            dma16(rq, lds + (uint32_t)(wave_u + kWaves * i) * 1024u, (uint32_t)(row * D * 2 + c * 16));
+        }
+    }
 
     // ---- tile loads, device memory -> LDS.  Load instruction t of a tile
     // fills LDS bytes [1024 t, 1024 t + 1024); lane i writes 16 bytes at
     // 1024 t + 16 i, i.e. physical chunk P = 64 t + i = row * CPR + chunk'.
     // The lane therefore fetches logical chunk chunk' ^ swz(row).
-    // kLoadWaves waves (all 8, or group B alone) issue the loads of a tile
-    // pair at the start of even phases; instruction t = w + kLoadWaves i
-    // comes from loader wave w.
-    constexpr int LW = kLoadWaves < TILE_INSTR ? kLoadWaves : TILE_INSTR;
+    // The waves of group A issue the loads of a tile pair at the end of
+    // their MFMA work in even phases (a load burst in front of the MFMAs
+    // stalls them); instruction t = w + LW i comes from wave w < LW.
+    constexpr int LW = 4 < TILE_INSTR ? 4 : TILE_INSTR;
     constexpr int DMA_HALF = TILE_INSTR / LW;     // loads per loader wave per tile
     constexpr int DMA_PER_PHASE = 2 * DMA_HALF;   // K tile + V tile
     static_assert(TILE_INSTR % LW == 0, "tile load split");
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int loader = kLoadWaves == kWaves ? wave_u : wave_u - (kWaves - kLoadWaves);
-    const bool is_loader = loader >= 0 && loader < LW;
+    const int loader = wave_u;
+    const bool is_loader = loader < LW;
     uint32_t voff[DMA_HALF];
 #pragma unroll
     for (int i = 0; i < DMA_HALF; ++i) {
@@ -272,6 +293,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         const int row = kb * 32 + l32;
         return *reinterpret_cast<const u32x4 *>(kt + row * D + (((2 * kk + g) ^ swz<D>(row)) * 8));
     };
+    // Q fragment (B operand of S^T) for k-step kk: query row rb*32 + l32 of
+    // the tile, dims 16 kk + 8 g .. +7.
+    auto frag_q = [&](int kk) -> u32x4 {
+        const int row = rb * 32 + l32;
+        return *reinterpret_cast<const u32x4 *>(sQ + row * D + (((2 * kk + g) ^ swz<D>(row)) * 8));
+    };
     // V^T fragment (A operand of P.V) for column block cb, 16-key chunk kc:
     // two transposing reads at rows 16 kc + 8 h + 4 g + (lane%16)/4, logical
     // chunk 4 cb + 2 ((lane/16)%2) + (lane%4)/2, 8-byte half lane%2; they
@@ -296,10 +323,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // the Q.K steps (per 32-key block, 4 k-steps each).  Fragments of step
     // s+1 are read from LDS before the MFMAs of step s are issued, so LDS
     // latency hides behind matrix-core work.
-    constexpr int QK_PER = DK < 4 ? DK : 4;            // MFMAs per Q.K step
-    constexpr int QK_STEPS_PER_KB = DK / QK_PER;
+    // A Q.K step covers two k-steps kk for both 32-key blocks: 4 MFMAs,
+    // 2 Q fragment reads shared by the two blocks, 4 K fragment reads.
+    constexpr int QK_STEPS = DK / 2;
+    constexpr int QK_PER = 4;                          // MFMAs per Q.K step
+    constexpr int QK_READS = 6;
     constexpr int PV_STEPS = DB;
-    constexpr int QK_STEPS = KB * QK_STEPS_PER_KB;
     auto load_step = [&](int st, const uint16_t *kt, const uint16_t *vt, bool do_pv, u32x4 *f) {
         if (st < PV_STEPS) {
             if (do_pv) {
@@ -307,11 +336,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                 for (int kc = 0; kc < 4; ++kc) f[kc] = frag_v(vt, st, kc);
             }
         } else {
-            const int q = st - PV_STEPS;
-            const int kb = q / QK_STEPS_PER_KB;
-            const int k0 = (q % QK_STEPS_PER_KB) * QK_PER;
+            const int k0 = 2 * (st - PV_STEPS);
 #pragma unroll
-            for (int i = 0; i < QK_PER; ++i) f[i] = frag_k(kt, kb, k0 + i);
+            for (int i = 0; i < 2; ++i) {
+                f[3 * i] = frag_q(k0 + i);
+                f[3 * i + 1] = frag_k(kt, 0, k0 + i);
+                f[3 * i + 2] = frag_k(kt, 1, k0 + i);
+            }
         }
     };
     auto mfma_step = [&](int st, bool do_pv, const u32x4 *f) {
@@ -322,27 +353,45 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                     oacc[st] = mfma32<BF16>(f[kc], pf[kc >> 1][kc & 1], oacc[st]);
             }
         } else {
-            const int q = st - PV_STEPS;
-            const int kb = q / QK_STEPS_PER_KB;
-            const int k0 = (q % QK_STEPS_PER_KB) * QK_PER;
 #pragma unroll
-            for (int i = 0; i < QK_PER; ++i) s[kb] = mfma32<BF16>(f[i], qf[k0 + i], s[kb]);
+            for (int i = 0; i < 2; ++i) {
+                s[0] = mfma32<BF16>(f[3 * i + 1], f[3 * i], s[0]);
+                s[1] = mfma32<BF16>(f[3 * i + 2], f[3 * i], s[1]);
+            }
         }
     };
     constexpr int NST = PV_STEPS + QK_STEPS;
-    auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, bool do_pv) {
+    // One branch-free block (P.V part on or off at compile time); the
+    // scheduling hints issue the reads of step s+1 between the MFMAs of
+    // step s rather than in one batch after them.
+    auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, auto pv_tag) {
+        constexpr bool DO_PV = decltype(pv_tag)::value;
+        constexpr int FIRST = DO_PV ? 0 : PV_STEPS;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        u32x4 f[2][4];
-        if (do_pv) load_step(0, kt, vt, true, f[0]);
-        else load_step(PV_STEPS, kt, vt, false, f[PV_STEPS & 1]);
+        u32x4 f[2][6];
+        load_step(FIRST, kt, vt, DO_PV, f[FIRST & 1]);
 #pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            if (st + 1 < NST) load_step(st + 1, kt, vt, do_pv, f[(st + 1) & 1]);
-            mfma_step(st, do_pv, f[st & 1]);
+        for (int st = FIRST; st < NST; ++st) {
+            if (st + 1 < NST) load_step(st + 1, kt, vt, DO_PV, f[(st + 1) & 1]);
+            mfma_step(st, DO_PV, f[st & 1]);
         }
+        if constexpr (DO_PV) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            sched_mfma_reads<4 * (PV_STEPS - 1), 2>();
+            sched_mfma_reads<2, 2>();
+            sched_mfma_reads<2, 1>();
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, QK_READS, 0);
+        }
+#pragma unroll
+        for (int rep_ = 0; rep_ < QK_STEPS - 1; ++rep_) {
+            sched_mfma_reads<2, 2>();
+            sched_mfma_reads<2, 1>();
+        }
+        sched_mfma_reads<QK_PER, 0>();
     };
 
     auto max3 = [](float a, float b, float c3) -> float {
@@ -419,7 +468,32 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     auto phase = [&](int ph, const uint16_t *k_cur, const uint16_t *v_prev,
                      uint16_t *k_next, uint16_t *v_cur) {
         const int j = ph >> 1;
-        // tile loads of this phase: K tile j+1 and V tile j, in even phases
+        const int t = ph - grp;
+        if (t >= 0) {
+            const int jj = t >> 1;
+            if ((t & 1) == 0) {
+                const bool do_pv = jj >= 1 && jj - 1 < n_w;
+                const bool do_qk = jj < n_w;
+                __builtin_amdgcn_s_setprio(1);
+                if (do_qk && do_pv) {
+                    mfma_phase(k_cur, v_prev, std::true_type{});
+                } else if (do_qk) {
+                    mfma_phase(k_cur, v_prev, std::false_type{});
+                } else if (do_pv) {
+                    u32x4 f[6];
+#pragma unroll
+                    for (int st = 0; st < PV_STEPS; ++st) {
+                        load_step(st, k_cur, v_prev, true, f);
+                        mfma_step(st, true, f);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+            } else if (jj < n_w) {
+                softmax(jj);
+            }
+        }
+        // tile loads of this phase: K tile j+1 and V tile j, by group A at the
+        // end of even phases
         if ((ph & 1) == 0 && is_loader) {
             const bool ld_k = j + 1 < n;
             const bool ld_v = j < n;
@@ -427,26 +501,6 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
             const i32x4 rv = tile_rsrc(Vp, ld_v ? j : 0);
 #pragma unroll
             for (int k = 0; k < DMA_PER_PHASE; ++k) issue_load(k, ld_k, ld_v, rk, rv, k_next, v_cur);
-        }
-        const int t = ph - grp;
-        if (t >= 0) {
-            const int jj = t >> 1;
-            if ((t & 1) == 0) {
-                const bool do_pv = jj >= 1 && jj - 1 < n_w;
-                const bool do_qk = jj < n_w;
-                if (do_qk) {
-                    mfma_phase(k_cur, v_prev, do_pv);
-                } else if (do_pv) {
-                    u32x4 f[4];
-#pragma unroll
-                    for (int st = 0; st < PV_STEPS; ++st) {
-                        load_step(st, k_cur, v_prev, true, f);
-                        mfma_step(st, true, f);
-                    }
-                }
-            } else if (jj < n_w) {
-                softmax(jj);
-            }
         }
         if (ph & 1) wait_tile_loads();
         barrier();
