@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep warming up until this much wall time has passed")
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -188,8 +190,16 @@ def main():
     def step():
         attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl, stream=stream)
 
-    for _ in range(args.warmup):
+    # Untimed warmup: W steps, continued until at least --warmup-seconds of
+    # GPU work has run, so that the clocks have left their idle state (the
+    # first tens of launches after an idle period run up to 25% slower).
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         step()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -227,7 +237,8 @@ def main():
     value = F / (ms_per_step / 1e3) / 1e12
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,

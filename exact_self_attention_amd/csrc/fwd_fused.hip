@@ -34,9 +34,13 @@
 //    query + 32*g, register r = key 8*(r/4) + 4*g + r%4) is the B operand of
 //    the P.V MFMA as it is; the transposing reads deliver V^T in the same key
 //    order.
-//  * Q stays in VGPRs.  exp2 with scale*log2(e) folded into one FMA; the
-//    running max is raised only when a tile's max exceeds it by more than
-//    2^8 (lazy rescale): the result is the same, probabilities stay < 256.
+//  * Q is staged in LDS once per workgroup.  exp2 with scale*log2(e) folded
+//    into one FMA.  Lazy running max: it moves only when a tile's max
+//    exceeds it by more than 2^8, and then a little above that max, so the
+//    output and normaliser are rarely rescaled; the result is the same and
+//    probabilities stay inside the fp16 range.  At d = 128 the exponentials
+//    are first taken against the running max as it stands, and the row max
+//    is only computed when a lane's tile sum exceeds 2^15 (rare).
 //  * Causal and key-padding masks: the loop stops at the last key tile any
 //    row of the workgroup can see, each wave skips tiles wholly after its
 //    rows, and per-element masking runs only on tiles that straddle a
@@ -70,7 +74,17 @@ constexpr int kQRows = 32;               // query rows per wave
 constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLazy = 8.0f;            // log2 of the largest unscaled probability
+// Lazy running max.  The running max only moves when a tile's max exceeds
+// it by more than kLazy (log2 units), and then to kHeadroom above that
+// tile's max, so that it rarely has to move again.  Probabilities stay below
+// 2^kLazy, and after a move the largest is 2^-kHeadroom.
+constexpr float kLazy = 8.0f;
+constexpr float kHeadroom = 8.0f;
+// At d = 128 the exponentials of a tile are taken against the running max as
+// it stands, before any row max is known; they are redone after a move only
+// when a lane's sum of the tile's probabilities exceeds kExpFirstBound
+// (below the fp16 maximum, so no probability can overflow).
+constexpr float kExpFirstBound = 32768.0f;
 // Buffer resource word 3 for raw (untyped) 32-bit loads on gfx9-class parts.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -283,7 +297,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
     f32x16 s[KB];
     u32x4 pf[KB][2];
-    float m_run = -INFINITY;  // running max of scale*log2(e)*score (possibly stale by < kLazy)
+    float m_run = -INFINITY;  // running max of scale*log2(e)*score (may trail the true one)
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
 
@@ -402,19 +416,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // Online softmax of tile j.  Masked scores become -inf; since c > 0 their
     // exp2 is exactly 0.  The row max and the row sum are trees (short
     // dependency chains); the normaliser sums the fp32 probabilities.
-    auto softmax = [&](int j) {
-        const int j0 = j * kBN;
-        const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool ok = key < Lk && (!CAUSAL || key <= my_q);
-                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                }
-        }
+    // Row max (over both lane halves) of the 32 scores a lane holds.
+    auto row_max = [&]() -> float {
         static_assert(KB == 2, "the reductions below assume 32 scores per lane");
         float t1[11];
 #pragma unroll
@@ -424,22 +427,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         t1[10] = fmaxf(s[1][14], s[1][15]);
         const float t2a = max3(t1[0], t1[1], t1[2]), t2b = max3(t1[3], t1[4], t1[5]);
         const float t2c = max3(t1[6], t1[7], t1[8]), t2d = fmaxf(t1[9], t1[10]);
-        float mx = max3(max3(t2a, t2b, t2c), t2d, t2d);
+        const float mx = max3(max3(t2a, t2b, t2c), t2d, t2d);
         const Halves mh = both_halves(mx);
-        mx = fmaxf(mh.lo, mh.hi);
-        const float m_tile = mx * c;  // -inf stays -inf (c > 0)
-        const bool grow = m_tile > m_run + kLazy;
-        if (__any(grow)) {
-            const float m_new = grow ? m_tile : m_run;
-            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        }
-        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+        return fmaxf(mh.lo, mh.hi);
+    };
+    // P = exp2(c s + neg_m) packed to 16 bits into pf; returns this lane's
+    // sum of the fp32 values (a tree, for short dependency chains).
+    auto exps = [&](float neg_m) -> float {
         float pr[32];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -456,7 +450,45 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
             for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
-        l_run += pr[0];
+        return pr[0];
+    };
+    auto softmax = [&](int j) {
+        const int j0 = j * kBN;
+        const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    const bool ok = key < Lk && (!CAUSAL || key <= my_q);
+                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
+                }
+        }
+        float lsum = 0.f;
+        bool max_first = true;
+        if (D >= 128 && j > 0) {
+            // exponentials first; a sum above the bound (or a row with no
+            // running max yet) sends the whole wave to the max-first path
+            lsum = exps(m_run == -INFINITY ? 0.f : -m_run);
+            max_first = __any(!(lsum <= kExpFirstBound) || m_run == -INFINITY);
+        }
+        if (max_first) {
+            const float m_tile = row_max() * c;  // -inf stays -inf (c > 0)
+            const bool grow = m_tile > m_run + kLazy;
+            if (__any(grow)) {
+                const float m_new = grow ? m_tile + kHeadroom : m_run;
+                const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+            }
+            lsum = exps(m_run == -INFINITY ? 0.f : -m_run);
+        }
+        l_run += lsum;
     };
 
     // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
