@@ -8,6 +8,7 @@ configuration whose throughput is reported as TFLOP/s and as a fraction of
 the dense fp16 matrix-core peak.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                  [--no-naive]
   python bench.py --copy-probe       # a plain device copy of known size, for
                                      # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle sample")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="skip timing the unfused attn_fwd_naive baseline")
     ap.add_argument("--copy-probe", action="store_true")
     return ap.parse_args()
 
@@ -111,6 +114,40 @@ def copy_probe():
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES,
                       "copy_probe_bytes_written": COPY_PROBE_BYTES, "launches": 5}))
+
+
+def naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F):
+    """Time the unfused attn_fwd_naive (scores and probabilities through HBM)
+    on the same inputs; its workspace holds at most 8 GiB of heads at once."""
+    per_head = attn.attn_fwd_naive_workspace_bytes(1, 1, w.N)
+    heads = max(1, min(w.B * w.H, (8 << 30) // per_head))
+    ws = torch.empty(heads * per_head // 4, dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+
+    def run():
+        attn.attn_fwd_naive(q, k, v, o, lse, workspace=ws, scale=scale, causal=w.causal,
+                            key_len=kl, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    once = time.perf_counter() - t0
+    reps = int(max(1, min(50, 1.0 / max(once, 1e-6))))
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    secs = ev0.elapsed_time(ev1) / 1e3 / reps
+    del ws
+    return {"value": F / secs / 1e12, "unit": "TFLOP/s", "ms_per_step": secs * 1e3,
+            "steps": reps, "kind": "attn_fwd_naive",
+            "workspace_heads_per_launch": heads}
 
 
 def cpu_baseline(w, case, target_s: float):
@@ -247,6 +284,10 @@ def main():
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
         "roofline": roof,
     }
+    if not args.no_naive:
+        nb = naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F)
+        nb["fused_speedup"] = nb["ms_per_step"] / ms_per_step
+        out["naive_baseline"] = nb
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, case, args.cpu_seconds)
     print(json.dumps(out), flush=True)
