@@ -73,6 +73,18 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQRows = 32;               // query rows per wave
 constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
+// K and V tiles each cycle through kRing LDS slots; a tile is fetched
+// kRing - 1 tiles ahead of its first use, so a load has 2 (kRing - 1) - 1
+// phases to arrive.
+constexpr int kRing = 3;
+constexpr int kAhead = kRing - 1;
+// Fragment reads run this many MFMA steps (of 4 MFMAs) ahead of their use.
+constexpr int kFragAhead = 1;
+// Tile loads are issued by all waves at the start of their softmax phases
+// when d >= this (the matrix-core phase is then the longer one), else by the
+// four waves of group A right after their matrix-core work in even phases
+// (the softmax phase is then the longer one).
+constexpr int kSpreadLoadsMinD = 128;
 constexpr float kLn2 = 0.69314718055994530942f;
 // Lazy running max.  The running max only moves when a tile's max exceeds
 // it by more than kLazy (log2 units), and then to kHeadroom above that
@@ -152,8 +164,34 @@ __device__ __forceinline__ void sched_mfma_reads() {
     }
 }
 
+// LDS reads of MFMA step st of a phase with PVS P.V steps out of NST: 8
+// transposing reads for a P.V step, 4 K fragment reads for a Q.K step.
+template <int NST, int PVS>
+constexpr int step_reads(int st) {
+    return st >= NST ? 0 : (st < PVS ? 8 : 4);
+}
+template <int A, int B, int NST, int PVS>
+constexpr int step_reads_upto() {
+    int n = 0;
+    for (int st = A; st < B; ++st) n += step_reads<NST, PVS>(st);
+    return n;
+}
+// Steps ST .. NST-1: each step's 4 MFMAs with the reads of step
+// ST + kFragAhead spread evenly between them.
+template <int ST, int NST, int PVS>
+__device__ __forceinline__ void sched_steps() {
+    if constexpr (ST < NST) {
+        sched_mfma_reads<4, step_reads<NST, PVS>(ST + kFragAhead) / 4>();
+        sched_steps<ST + 1, NST, PVS>();
+    }
+}
+
+// Waits until at most KEEP of this wave's vector-memory loads are still in
+// flight (loads complete in issue order).
+template <int KEEP>
 __device__ __forceinline__ void wait_tile_loads() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(KEEP >= 0 && KEEP < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -189,10 +227,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int DB = D / 32;                    // 32-wide column blocks of O
 
     __shared__ __attribute__((aligned(1024))) uint16_t sQ[kBM * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[kRing][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[kRing][TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -254,38 +290,51 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // fills LDS bytes [1024 t, 1024 t + 1024); lane i writes 16 bytes at
     // 1024 t + 16 i, i.e. physical chunk P = 64 t + i = row * CPR + chunk'.
     // The lane therefore fetches logical chunk chunk' ^ swz(row).
-    // The waves of group A issue the loads of a tile pair at the end of
-    // their MFMA work in even phases (a load burst in front of the MFMAs
-    // stalls them); instruction t = w + LW i comes from wave w < LW.
-    constexpr int LW = 4 < TILE_INSTR ? 4 : TILE_INSTR;
-    constexpr int DMA_HALF = TILE_INSTR / LW;     // loads per loader wave per tile
-    constexpr int DMA_PER_PHASE = 2 * DMA_HALF;   // K tile + V tile
-    static_assert(TILE_INSTR % LW == 0, "tile load split");
-    const int loader = wave_u;
-    const bool is_loader = loader < LW;
-    uint32_t voff[DMA_HALF];
+    // Batch jb is K tile jb + kAhead and V tile jb + kAhead - 1 (2 TILE_INSTR
+    // instructions); each of the NLD loader waves issues SHARE of them,
+    // instruction t = wave + NLD i (K for t < TILE_INSTR, then V).  Issuing a
+    // 1 KB load can stall the issuing wave while the vector memory front end
+    // is busy, so the loads go where a wave has slack (see kSpreadLoads).
+    constexpr bool kSpreadLoads = D >= kSpreadLoadsMinD;
+    constexpr int BATCH = 2 * TILE_INSTR;
+    constexpr int NLD = kSpreadLoads ? kWaves : kWaves / 2;
+    constexpr int SHARE = BATCH / NLD;             // loads per loader per batch
+    static_assert(BATCH % NLD == 0, "tile load split");
+    const bool is_loader = wave_u < NLD;
+    uint32_t voff[SHARE];
+    uint32_t lds_off[SHARE];
+    bool ld_is_v[SHARE];
 #pragma unroll
-    for (int i = 0; i < DMA_HALF; ++i) {
-        const int t = (is_loader ? loader : 0) + LW * i;
-        const int P = 64 * t + lane;
+    for (int i = 0; i < SHARE; ++i) {
+        const int t = (is_loader ? wave_u : 0) + NLD * i;
+        const int tt = t % TILE_INSTR;
+        ld_is_v[i] = t >= TILE_INSTR;
+        lds_off[i] = (uint32_t)tt * 1024u;
+        const int P = 64 * tt + lane;
         const int row = P / CPR;
         const int c = (P % CPR) ^ swz<D>(row);
         voff[i] = (uint32_t)(row * D * 2 + c * 16);
     }
+    // Buffer over key tile j, clipped at the last valid key; a tile at or
+    // past the workgroup's last one gets an empty range, so its loads write
+    // zeros to LDS without touching memory (and every batch has the same
+    // number of instructions, which the waits below count on).
     auto tile_rsrc = [&](const uint16_t *src, int j) -> i32x4 {
         const int j0 = j * kBN;
-        const int rows = min(kBN, Lk - j0);
-        return make_rsrc(src + (size_t)j0 * D, (uint32_t)(rows * D * 2));
+        const int rows = j < n ? min(kBN, Lk - j0) : 0;
+        return make_rsrc(src + (size_t)(j < n ? j0 : 0) * D, (uint32_t)(rows * D * 2));
     };
-    // Load k (0 <= k < DMA_PER_PHASE) of this loader wave: K tile, then V.
-    auto issue_load = [&](int k, bool ld_k, bool ld_v, const i32x4 &rk, const i32x4 &rv,
-                          uint16_t *k_dst, uint16_t *v_dst) {
-        const int i = k % DMA_HALF;
-        const uint32_t t = (uint32_t)(loader + LW * i);
-        if (k < DMA_HALF) {
-            if (ld_k) dma16(rk, (uint32_t)(uintptr_t)(lds_void *)k_dst + t * 1024u, voff[i]);
-        } else {
-            if (ld_v) dma16(rv, (uint32_t)(uintptr_t)(lds_void *)v_dst + t * 1024u, voff[i]);
+    auto issue_batch = [&](int jb, const uint16_t *k_dst, const uint16_t *v_dst) {
+        const i32x4 rk = tile_rsrc(Kp, jb + kAhead);
+        const i32x4 rv = tile_rsrc(Vp, jb + kAhead - 1);
+        const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)k_dst;
+        const uint32_t vl = (uint32_t)(uintptr_t)(lds_void *)v_dst;
+#pragma unroll
+        for (int i = 0; i < SHARE; ++i) {
+            if (ld_is_v[i])
+                dma16(rv, vl + lds_off[i], voff[i]);
+            else
+                dma16(rk, kl + lds_off[i], voff[i]);
         }
     };
 
@@ -332,80 +381,70 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         return (u32x4){lo[0], lo[1], hi[0], hi[1]};
     };
 
-    // MFMA work of one phase as a list of steps of up to 4 MFMAs: first the
-    // P.V steps (one per 32-column block of O, over the 4 key chunks), then
-    // the Q.K steps (per 32-key block, 4 k-steps each).  Fragments of step
-    // s+1 are read from LDS before the MFMAs of step s are issued, so LDS
-    // latency hides behind matrix-core work.
-    // A Q.K step covers two k-steps kk for both 32-key blocks: 4 MFMAs,
-    // 2 Q fragment reads shared by the two blocks, 4 K fragment reads.
+    // MFMA work of one phase as a list of steps of 4 MFMAs each: first the
+    // P.V steps (one per 32-column block of O, over the 4 key chunks: 8
+    // transposing reads), then the Q.K steps (two k-steps for both 32-key
+    // blocks: 4 K fragment reads; the Q fragments sit in VGPRs).  The
+    // fragments of step s + kFragAhead are read while the MFMAs of step s
+    // issue, from a ring of kFragAhead + 1 fragment sets, so each read has
+    // kFragAhead steps of matrix-core work to arrive in.
     constexpr int QK_STEPS = DK / 2;
-    constexpr int QK_PER = 4;                          // MFMAs per Q.K step
-    constexpr int QK_READS = 6;
     constexpr int PV_STEPS = DB;
-    auto load_step = [&](int st, const uint16_t *kt, const uint16_t *vt, bool do_pv, u32x4 *f) {
+    constexpr int NST = PV_STEPS + QK_STEPS;
+    u32x4 qreg[DK];
+    auto load_step = [&](int st, const uint16_t *kt, const uint16_t *vt, u32x4 *f) {
         if (st < PV_STEPS) {
-            if (do_pv) {
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) f[kc] = frag_v(vt, st, kc);
-            }
+            for (int kc = 0; kc < 4; ++kc) f[kc] = frag_v(vt, st, kc);
         } else {
             const int k0 = 2 * (st - PV_STEPS);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                f[3 * i] = frag_q(k0 + i);
-                f[3 * i + 1] = frag_k(kt, 0, k0 + i);
-                f[3 * i + 2] = frag_k(kt, 1, k0 + i);
+                f[2 * i] = frag_k(kt, 0, k0 + i);
+                f[2 * i + 1] = frag_k(kt, 1, k0 + i);
             }
         }
     };
-    auto mfma_step = [&](int st, bool do_pv, const u32x4 *f) {
+    auto mfma_step = [&](int st, const u32x4 *f) {
         if (st < PV_STEPS) {
-            if (do_pv) {
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    oacc[st] = mfma32<BF16>(f[kc], pf[kc >> 1][kc & 1], oacc[st]);
-            }
+            for (int kc = 0; kc < 4; ++kc)
+                oacc[st] = mfma32<BF16>(f[kc], pf[kc >> 1][kc & 1], oacc[st]);
         } else {
+            const int k0 = 2 * (st - PV_STEPS);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                s[0] = mfma32<BF16>(f[3 * i + 1], f[3 * i], s[0]);
-                s[1] = mfma32<BF16>(f[3 * i + 2], f[3 * i], s[1]);
+                s[0] = mfma32<BF16>(f[2 * i], qreg[k0 + i], s[0]);
+                s[1] = mfma32<BF16>(f[2 * i + 1], qreg[k0 + i], s[1]);
             }
         }
     };
-    constexpr int NST = PV_STEPS + QK_STEPS;
-    // One branch-free block (P.V part on or off at compile time); the
-    // scheduling hints issue the reads of step s+1 between the MFMAs of
-    // step s rather than in one batch after them.
-    auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, auto pv_tag) {
+    // One branch-free block (P.V and Q.K parts on or off at compile time);
+    // the scheduling hints place the reads of step s + kFragAhead between
+    // the MFMAs of step s.
+    auto mfma_phase = [&](const uint16_t *kt, const uint16_t *vt, auto pv_tag, auto qk_tag) {
         constexpr bool DO_PV = decltype(pv_tag)::value;
+        constexpr bool DO_QK = decltype(qk_tag)::value;
         constexpr int FIRST = DO_PV ? 0 : PV_STEPS;
+        constexpr int LAST = DO_QK ? NST : PV_STEPS;
+        constexpr int NF = kFragAhead + 1;
+        if constexpr (DO_QK) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        u32x4 f[2][6];
-        load_step(FIRST, kt, vt, DO_PV, f[FIRST & 1]);
-#pragma unroll
-        for (int st = FIRST; st < NST; ++st) {
-            if (st + 1 < NST) load_step(st + 1, kt, vt, DO_PV, f[(st + 1) & 1]);
-            mfma_step(st, DO_PV, f[st & 1]);
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
         }
-        if constexpr (DO_PV) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-            sched_mfma_reads<4 * (PV_STEPS - 1), 2>();
-            sched_mfma_reads<2, 2>();
-            sched_mfma_reads<2, 1>();
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x100, QK_READS, 0);
-        }
+        u32x4 f[NF][4];
 #pragma unroll
-        for (int rep_ = 0; rep_ < QK_STEPS - 1; ++rep_) {
-            sched_mfma_reads<2, 2>();
-            sched_mfma_reads<2, 1>();
+        for (int st = FIRST; st < FIRST + kFragAhead; ++st)
+            if (st < LAST) load_step(st, kt, vt, f[st % NF]);
+#pragma unroll
+        for (int st = FIRST; st < LAST; ++st) {
+            if (st + kFragAhead < LAST) load_step(st + kFragAhead, kt, vt, f[(st + kFragAhead) % NF]);
+            mfma_step(st, f[st % NF]);
         }
-        sched_mfma_reads<QK_PER, 0>();
+        __builtin_amdgcn_sched_group_barrier(0x100, step_reads_upto<FIRST, FIRST + kFragAhead, LAST, PV_STEPS>(), 0);
+        sched_steps<FIRST, LAST, PV_STEPS>();
     };
 
     auto max3 = [](float a, float b, float c3) -> float {
@@ -494,11 +533,17 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
     // and the softmax of tile j in phase 2j+1; group B runs one phase later.
     // K tile j is read in phases 2j and 2j+1, V tile j in 2j+2 and 2j+3.
-    // Tile loads for K j+1 and V j start at phase 2j and are waited for at
-    // the end of phase 2j+1.  Slot arrays are passed in statically so the
+    // Batch j (K tile j+kAhead, V tile j+kAhead-1, both first read in phase
+    // 2(j+kAhead)) is issued in phase 2j (group A, after its matrix-core
+    // work) or, with kSpreadLoads, by group B in phase 2j and group A in
+    // phase 2j+1 (at the start of their softmax of tile j).  It is waited for
+    // at the end of phase 2(j+kAhead)-1, when each loader's share of the
+    // kAhead-1 later batches may still be in flight.  Its slots were last
+    // read in phase 2j-1.  Slot arrays are passed in statically so the
     // compiler can tell the in-flight loads from the tiles being read.
     auto phase = [&](int ph, const uint16_t *k_cur, const uint16_t *v_prev,
-                     uint16_t *k_next, uint16_t *v_cur) {
+                     const uint16_t *k_next, const uint16_t *v_next) {
+        if (kSpreadLoads && (ph & 1) != grp) issue_batch(ph >> 1, k_next, v_next);
         const int j = ph >> 1;
         const int t = ph - grp;
         if (t >= 0) {
@@ -508,57 +553,57 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                 const bool do_qk = jj < n_w;
                 __builtin_amdgcn_s_setprio(1);
                 if (do_qk && do_pv) {
-                    mfma_phase(k_cur, v_prev, std::true_type{});
+                    mfma_phase(k_cur, v_prev, std::true_type{}, std::true_type{});
                 } else if (do_qk) {
-                    mfma_phase(k_cur, v_prev, std::false_type{});
+                    mfma_phase(k_cur, v_prev, std::false_type{}, std::true_type{});
                 } else if (do_pv) {
-                    u32x4 f[6];
-#pragma unroll
-                    for (int st = 0; st < PV_STEPS; ++st) {
-                        load_step(st, k_cur, v_prev, true, f);
-                        mfma_step(st, true, f);
-                    }
+                    mfma_phase(k_cur, v_prev, std::true_type{}, std::false_type{});
                 }
                 __builtin_amdgcn_s_setprio(0);
             } else if (jj < n_w) {
                 softmax(jj);
             }
         }
-        // tile loads of this phase: K tile j+1 and V tile j, by group A at the
-        // end of even phases
-        if ((ph & 1) == 0 && is_loader) {
-            const bool ld_k = j + 1 < n;
-            const bool ld_v = j < n;
-            const i32x4 rk = tile_rsrc(Kp, ld_k ? j + 1 : 0);
-            const i32x4 rv = tile_rsrc(Vp, ld_v ? j : 0);
-#pragma unroll
-            for (int k = 0; k < DMA_PER_PHASE; ++k) issue_load(k, ld_k, ld_v, rk, rv, k_next, v_cur);
-        }
-        if (ph & 1) wait_tile_loads();
+        if (!kSpreadLoads && (ph & 1) == 0 && is_loader) issue_batch(ph >> 1, k_next, v_next);
+        if (ph & 1) wait_tile_loads<(kAhead - 1) * SHARE>();
         barrier();
     };
 
-    // prologue: K tile 0
-    if (n > 0) {
+    // prologue: K tile 0, then the batches of the virtual phases -2(kAhead-1)
+    // .. -2 (K tiles 1 .. kAhead-1 and V tiles 0 .. kAhead-2); only K tile 0
+    // (and the Q tile) must have arrived before the first phase.
+    const int n_phases = n > 0 ? 2 * n + 2 : 0;
+    if (n > 0 && is_loader) {
         const i32x4 rk = tile_rsrc(Kp, 0);
-        if (is_loader) {
+        const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)sK[0];
 #pragma unroll
-            for (int k = 0; k < DMA_HALF; ++k) issue_load(k, true, false, rk, rk, sK0, sV0);
-        }
-        wait_tile_loads();
+        for (int i = 0; i < SHARE; ++i)
+            if (!ld_is_v[i]) dma16(rk, kl + lds_off[i], voff[i]);
+#pragma unroll
+        for (int jb = 1 - kAhead; jb < 0; ++jb)
+            issue_batch(jb, sK[(jb + kAhead) % kRing], sV[(jb + kAhead - 1) % kRing]);
+        wait_tile_loads<(kAhead - 1) * SHARE>();
+    } else {
+        wait_tile_loads<0>();
     }
     barrier();
 
-    // Phases 4i .. 4i+3 handle tiles j = 2i (slots 0) and j = 2i+1 (slots 1).
-    // For group B the "current" tile of an odd phase 2j+1 is tile j as well,
-    // so the slot arguments depend only on the phase.
-    const int n_phases = n > 0 ? 2 * n + 2 : 0;
-    for (int ph = 0; ph < n_phases; ph += 4) {
-        phase(ph + 0, sK0, sV1, sK1, sV0);
-        if (ph + 1 < n_phases) phase(ph + 1, sK0, sV1, sK1, sV0);
-        if (ph + 2 < n_phases) phase(ph + 2, sK1, sV0, sK0, sV1);
-        if (ph + 3 < n_phases) phase(ph + 3, sK1, sV0, sK0, sV1);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) qreg[kk] = frag_q(kk);
+
+    // Phases 2 kRing i + 2u and + 1 handle tile j = kRing i + u, whose K tile
+    // sits in slot u; slots therefore depend only on the unrolled position.
+    for (int ph = 0; ph < n_phases; ph += 2 * kRing) {
+#pragma unroll
+        for (int u = 0; u < 2 * kRing; ++u) {
+            const int t = u >> 1;
+            if (ph + u < n_phases)
+                phase(ph + u, sK[t], sV[(t + kRing - 1) % kRing], sK[(t + kAhead) % kRing],
+                      sV[(t + kAhead - 1) % kRing]);
+        }
     }
+    // loads of tiles past the last one (empty ranges) may still be in flight
+    wait_tile_loads<0>();
 
     // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l)
     const Halves lh = both_halves(l_run);
