@@ -191,7 +191,7 @@ attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N, int
     if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (N < 0 || N > kMaxN) return ATTN_ERR_INVALID_ARG;
     if (buf == nullptr || buf_len == 0) return ATTN_ERR_INVALID_ARG;
-    std::snprintf(buf, buf_len, "%s", attn::fwd_kernel_name(dtype == ATTN_BF16, (int)d, causal != 0));
+    std::snprintf(buf, buf_len, "%s", attn::fwd_kernel_name(dtype == ATTN_BF16, (int)d, causal != 0, N));
     return ATTN_OK;
 }
 

@@ -51,28 +51,17 @@
 
 #include <type_traits>
 
+#include "cdna4.h"
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace cdna4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQRows = 32;               // query rows per wave
 constexpr int kBM = kWaves * kQRows;     // query rows per workgroup
-constexpr int kBN = 64;                  // keys per tile
 // K and V tiles each cycle through kRing LDS slots; a tile is fetched
 // kRing - 1 tiles ahead of its first use, so a load has 2 (kRing - 1) - 1
 // phases to arrive.
@@ -85,74 +74,11 @@ constexpr int kFragAhead = 1;
 // four waves of group A right after their matrix-core work in even phases
 // (the softmax phase is then the longer one).
 constexpr int kSpreadLoadsMinD = 128;
-constexpr float kLn2 = 0.69314718055994530942f;
-// Lazy running max.  The running max only moves when a tile's max exceeds
-// it by more than kLazy (log2 units), and then to kHeadroom above that
-// tile's max, so that it rarely has to move again.  Probabilities stay below
-// 2^kLazy, and after a move the largest is 2^-kHeadroom.
-constexpr float kLazy = 8.0f;
-constexpr float kHeadroom = 8.0f;
 // At d = 128 the exponentials of a tile are taken against the running max as
 // it stands, before any row max is known; they are redone after a move only
 // when a lane's sum of the tile's probabilities exceeds kExpFirstBound
 // (below the fp16 maximum, so no probability can overflow).
 constexpr float kExpFirstBound = 32768.0f;
-// Buffer resource word 3 for raw (untyped) 32-bit loads on gfx9-class parts.
-constexpr int kBufferWord3 = 0x00020000;
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-    if constexpr (BF16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Two floats -> two 16-bit values (round to nearest even), low half first.
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    f32x2 v = {lo, hi};
-    if constexpr (BF16)
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    else
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// The values of x in lanes l % 32 and l % 32 + 32, for every lane l:
-// v_permlane32_swap of x with itself leaves the low half of the wave in
-// both halves of the first result and the high half in the second.
-struct Halves {
-    float lo, hi;
-};
-__device__ __forceinline__ Halves both_halves(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
-}
-
-// XOR swizzle of the 16-byte chunk index within row `row` of a tile with D
-// halves per row.  It makes (a) the 128-bit fragment reads of 16
-// consecutive rows at one logical chunk and (b) the transposing 8-byte reads
-// of 4 consecutive rows x 4 consecutive chunks land in distinct bank groups.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-    else return (row >> 2) & 3;
-}
-
-// Workgroup barrier without the memory-model waits of __syncthreads: the
-// code orders its LDS traffic itself (fragment reads are consumed before the
-// barrier; tile loads are waited for explicitly).
-__device__ __forceinline__ void barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // Scheduling pattern: N times (one MFMA, then R LDS reads).
 template <int N, int R>
@@ -184,37 +110,6 @@ __device__ __forceinline__ void sched_steps() {
         sched_mfma_reads<4, step_reads<NST, PVS>(ST + kFragAhead) / 4>();
         sched_steps<ST + 1, NST, PVS>();
     }
-}
-
-// Waits until at most KEEP of this wave's vector-memory loads are still in
-// flight (loads complete in issue order).
-template <int KEEP>
-__device__ __forceinline__ void wait_tile_loads() {
-    static_assert(KEEP >= 0 && KEEP < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource (gfx9 layout) over nbytes bytes at base, stride 0.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t nbytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
-    r[3] = kBufferWord3;
-    return r;
-}
-
-// One wave-wide tile load: lane i copies the 16 bytes at byte offset voff of
-// the buffer into LDS at lds_addr + 16 i; bytes past the buffer range read
-// as zero.  Written as inline assembly so that the compiler does not add
-// waits for these loads before unrelated LDS reads: the kernel waits for
-// them itself (wait_tile_loads) before the barrier that publishes a tile.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 template <int D, bool BF16, bool CAUSAL>
@@ -350,35 +245,14 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
 
-    // K fragment (A operand of S^T) for 32-key block kb, k-step kk: key row
-    // kb*32 + l32, dims 16 kk + 8 g .. +7, one 128-bit read.
     auto frag_k = [&](const uint16_t *kt, int kb, int kk) -> u32x4 {
-        const int row = kb * 32 + l32;
-        return *reinterpret_cast<const u32x4 *>(kt + row * D + (((2 * kk + g) ^ swz<D>(row)) * 8));
+        return cdna4::frag_k<D>(kt, kb, kk, l32, g);
     };
     // Q fragment (B operand of S^T) for k-step kk: query row rb*32 + l32 of
-    // the tile, dims 16 kk + 8 g .. +7.
-    auto frag_q = [&](int kk) -> u32x4 {
-        const int row = rb * 32 + l32;
-        return *reinterpret_cast<const u32x4 *>(sQ + row * D + (((2 * kk + g) ^ swz<D>(row)) * 8));
-    };
-    // V^T fragment (A operand of P.V) for column block cb, 16-key chunk kc:
-    // two transposing reads at rows 16 kc + 8 h + 4 g + (lane%16)/4, logical
-    // chunk 4 cb + 2 ((lane/16)%2) + (lane%4)/2, 8-byte half lane%2; they
-    // return V[16kc + 8h + 4g + t][32 cb + l32] for t = 0..3, the key order
-    // of the P registers.
+    // the tile, dims 16 kk + 8 g .. +7 (same layout as a K fragment).
+    auto frag_q = [&](int kk) -> u32x4 { return cdna4::frag_k<D>(sQ, rb, kk, l32, g); };
     auto frag_v = [&](const uint16_t *vt, int cb, int kc) -> u32x4 {
-        i16x4 part[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 16 * kc + 8 * h + 4 * g + (lane & 15) / 4;
-            const int chunk = (4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ swz<D>(row);
-            part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(vt + row * D + chunk * 8 + (lane & 1) * 4));
-        }
-        const u32x2 lo = __builtin_bit_cast(u32x2, part[0]);
-        const u32x2 hi = __builtin_bit_cast(u32x2, part[1]);
-        return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        return cdna4::frag_v<D>(vt, cb, kc, lane, g);
     };
 
     // MFMA work of one phase as a list of steps of 4 MFMAs each: first the
@@ -447,50 +321,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         sched_steps<FIRST, LAST, PV_STEPS>();
     };
 
-    auto max3 = [](float a, float b, float c3) -> float {
-        float d;
-        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c3));
-        return d;
-    };
     // Online softmax of tile j.  Masked scores become -inf; since c > 0 their
     // exp2 is exactly 0.  The row max and the row sum are trees (short
     // dependency chains); the normaliser sums the fp32 probabilities.
-    // Row max (over both lane halves) of the 32 scores a lane holds.
-    auto row_max = [&]() -> float {
-        static_assert(KB == 2, "the reductions below assume 32 scores per lane");
-        float t1[11];
-#pragma unroll
-        for (int i = 0; i < 10; ++i)
-            t1[i] = max3(s[(3 * i) / 16][(3 * i) % 16], s[(3 * i + 1) / 16][(3 * i + 1) % 16],
-                         s[(3 * i + 2) / 16][(3 * i + 2) % 16]);
-        t1[10] = fmaxf(s[1][14], s[1][15]);
-        const float t2a = max3(t1[0], t1[1], t1[2]), t2b = max3(t1[3], t1[4], t1[5]);
-        const float t2c = max3(t1[6], t1[7], t1[8]), t2d = fmaxf(t1[9], t1[10]);
-        const float mx = max3(max3(t2a, t2b, t2c), t2d, t2d);
-        const Halves mh = both_halves(mx);
-        return fmaxf(mh.lo, mh.hi);
-    };
-    // P = exp2(c s + neg_m) packed to 16 bits into pf; returns this lane's
-    // sum of the fp32 values (a tree, for short dependency chains).
-    auto exps = [&](float neg_m) -> float {
-        float pr[32];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int i = kb * 16 + ch * 8 + 2 * w;
-                    pr[i] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w], c, neg_m));
-                    pr[i + 1] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w + 1], c, neg_m));
-                    pf[kb][ch][w] = pack2<BF16>(pr[i], pr[i + 1]);
-                }
-#pragma unroll
-        for (int w = 16; w >= 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
-        return pr[0];
-    };
+    static_assert(KB == 2, "the softmax arithmetic assumes 64-key tiles");
+    auto row_max = [&]() -> float { return row_max64(s); };
+    auto exps = [&](float neg_m) -> float { return exps64<BF16>(s, c, neg_m, pf); };
     auto softmax = [&](int j) {
         const int j0 = j * kBN;
         const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
@@ -671,11 +507,11 @@ const FwdEntry &entry(bool bf16, int d, bool causal) {
 }
 }  // namespace
 
-int fwd_query_tile(int) { return kBM; }
+const char *fwd_fused_kernel_name(bool bf16, int d, bool causal) {
+    return entry(bf16, d, causal).name;
+}
 
-const char *fwd_kernel_name(bool bf16, int d, bool causal) { return entry(bf16, d, causal).name; }
-
-hipError_t launch_fwd(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
+hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
     p.n_qtiles = (int)((p.N + kBM - 1) / kBM);
     const int64_t blocks = (int64_t)p.n_qtiles * p.BH;
     if (blocks <= 0) return hipSuccess;

@@ -22,13 +22,22 @@ struct FwdParams {
     float scale_log2;           // scale * log2(e), > 0
 };
 
-// Query rows each fused workgroup owns (the query tile height).
-int fwd_query_tile(int d);
-// Launches the fused kernel instance for (bf16, d, causal).  p.n_qtiles is
-// filled in here.
+// Streaming kernel (any N): 8 waves, 256 query rows per workgroup, K/V
+// tiles through LDS rings, matrix-core and softmax phases ping-ponging
+// between two wave groups.  p.n_qtiles is filled in here.
+hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
+const char *fwd_fused_kernel_name(bool bf16, int d, bool causal);
+
+// Short-sequence kernel (N <= fwd_short_max_keys(d)): 4 waves, 128 query
+// rows per workgroup, the head's whole K and V resident in LDS.
+int64_t fwd_short_max_keys(int d);
+hipError_t launch_fwd_short(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
+const char *fwd_short_kernel_name(bool bf16, int d, bool causal);
+
+// Dispatch on (dtype, d, N, causal): the kernel attn_fwd launches, and its
+// name as profilers report it.
 hipError_t launch_fwd(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
-// Name of that instance, as profilers report it.
-const char *fwd_kernel_name(bool bf16, int d, bool causal);
+const char *fwd_kernel_name(bool bf16, int d, bool causal, int64_t N);
 
 // Arguments of the unfused baseline, for heads [bh0, bh0 + nbh).
 struct NaiveParams {

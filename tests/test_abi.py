@@ -54,7 +54,12 @@ def test_workspace_bytes(lib):
 def test_kernel_names(lib):
     assert lib.attn_fwd_kernel_name(0, 128, 4096, True, False) == "attn_fwd_d128_f16_causal"
     assert lib.attn_fwd_kernel_name(1, 64, 2048, False, False) == "attn_fwd_d64_bf16_full"
-    assert lib.attn_fwd_kernel_name(0, 32, 256, False, True) == "attn_fwd_d32_f16_full"
+    # a head whose keys fit in LDS goes to the short-sequence kernel
+    assert lib.attn_fwd_kernel_name(0, 32, 256, False, True) == "attn_fwd_short_d32_f16_full"
+    assert lib.attn_fwd_kernel_name(0, 32, 257, False, True) == "attn_fwd_d32_f16_full"
+    assert lib.attn_fwd_kernel_name(1, 64, 256, True, False) == "attn_fwd_short_d64_bf16_causal"
+    assert lib.attn_fwd_kernel_name(0, 128, 128, False, False) == "attn_fwd_short_d128_f16_full"
+    assert lib.attn_fwd_kernel_name(0, 128, 129, False, False) == "attn_fwd_d128_f16_full"
     with pytest.raises(lib.AttnError):
         lib.attn_fwd_kernel_name(0, 48, 256, False, False)
 
