@@ -186,3 +186,33 @@ def test_output_written_only_inside_bounds():
     torch.cuda.synchronize()
     assert torch.all(buf[:1024] == -7.0) and torch.all(buf[1024 + n_o:] == -7.0)
     assert torch.all(lbuf[:64] == 3.5) and torch.all(lbuf[64 + 2 * 131:] == 3.5)
+
+
+# Shapes with more 256-row query tiles than resident workgroups, so every
+# workgroup of the streaming kernel processes several items back to back;
+# key lengths mix full, short (padded items of fewer than 4 tiles), one and
+# zero.  Every row is checked.
+STREAM_CASES = [
+    # (B, H, N, d, causal, dtype)
+    (24, 16, 700, 128, True, ai.F16),
+    (24, 16, 700, 128, False, ai.BF16),
+    (48, 12, 520, 64, False, ai.BF16),
+    (48, 12, 520, 64, True, ai.F16),
+    (64, 12, 300, 32, False, ai.F16),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dtype", STREAM_CASES,
+                         ids=[f"B{b}H{h}N{n}d{d}{'c' if c else 'f'}{t}" for b, h, n, d, c, t in STREAM_CASES])
+def test_streaming_many_items_per_workgroup(B, H, N, d, causal, dtype):
+    seed = 20_000 + B + H + N + d + causal
+    rng = np.random.default_rng(seed)
+    kl = rng.integers(0, N + 1, size=B)
+    kl[:4] = [N, 1, 0, 70]
+    case = ai.random_case(B, H, N, d, dtype, seed=seed, sigma=1.5, key_len=[int(x) for x in kl])
+    gu.log(f"stream B={B} H={H} N={N} d={d} causal={causal} {dtype}")
+    O, LSE = gu.run_fused(case, causal)
+    sel = ai.all_rows_selection(B, H, N)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"stream B={B} H={H} N={N} d={d} causal={causal}", sel)
