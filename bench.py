@@ -2,13 +2,14 @@
 """Benchmark of the fused exact-attention forward on one MI355X.
 
 A step is one attn_fwd launch over one batch of seeded synthetic inputs that
-are already resident in device memory.  The default workload is the causal
+are already resident in device memory.  The K timed steps are recorded into
+one HIP graph and replayed, so no host time separates the launches.  The default workload is the causal
 decoder prefill B=1 H=32 N=4096 d=128 fp16 (scale 1/sqrt(128)), the
 configuration whose throughput is reported as TFLOP/s and as a fraction of
 the dense fp16 matrix-core peak.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--no-naive]
+                  [--no-naive] [--no-graph]
   python bench.py --copy-probe       # a plain device copy of known size, for
                                      # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
@@ -30,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal ×½) + % of MI355X MFMA peak"
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "exact_self_attention_amd", "csrc", "fwd_fused.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_self_attention_amd", "csrc", f)
+                  for f in ("cdna4.h", "dispatch.cpp", "fwd_fused.hip", "fwd_short.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 COPY_PROBE_BYTES = 1 << 30
 
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle sample")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time K plain launches instead of one replay of a graph of K launches")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the unfused attn_fwd_naive baseline")
     ap.add_argument("--copy-probe", action="store_true")
@@ -84,8 +88,12 @@ def algorithmic_bytes(w, key_len=None) -> int:
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the fused-kernel sources, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str):
@@ -222,10 +230,10 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     scale = float(w.scale)
-    stream = torch.cuda.current_stream(dev)
 
     def step():
-        attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl, stream=stream)
+        # on the current stream (the capture stream while a graph records)
+        attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
 
     # Untimed warmup: W steps, continued until at least --warmup-seconds of
     # GPU work has run, so that the clocks have left their idle state (the
@@ -238,13 +246,30 @@ def main():
         if n_warm % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # The K timed steps: recorded once into a HIP graph and replayed, so the
+    # launches run back to back with no host time between them (a short
+    # kernel is otherwise shorter than one Python-side launch); --no-graph
+    # times K plain launches instead.
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -275,6 +300,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "launch": "plain" if args.no_graph else "hip_graph",
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
