@@ -30,6 +30,11 @@ The five workloads follow the shapes the pages measure or describe:
 * ``long_context``: B=1 H=32 N=32768 d=128 bf16, causal (the longest sequence
   of the portfolio page's benchmark table); the oracle checks 256 seeded
   query rows per head.
+
+One more workload measures the split-key forward:
+
+* ``prefill_shard8``: B=1 H=4 N=4096 d=128 fp16, causal: the prefill's
+  per-GPU share when its 32 heads are divided among 8 GPUs.
 """
 from __future__ import annotations
 
@@ -79,8 +84,14 @@ WORKLOADS = {
                       q_sigma=3.0, k_sigma=3.0, seed=1004),
     "long_context": Workload("long_context", 1, 32, 32768, 128, BF16, True, False,
                              seed=1005, sample_rows=256),
+    # The prefill's per-GPU share when its 32 heads are split 8 ways: 4 heads,
+    # too few 256-row query tiles (64) to occupy the GPU, the shape the
+    # split-key forward is for.
+    "prefill_shard8": Workload("prefill_shard8", 1, 4, 4096, 128, F16, True, False, seed=1006),
 }
 WORKLOAD_ORDER = ["single_head", "reranker", "prefill", "peaky", "long_context"]
+# workloads beyond the five the pages' configurations describe
+EXTRA_WORKLOADS = ["prefill_shard8"]
 
 
 # ---------------------------------------------------------------- rounding

@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle sample")
+    ap.add_argument("--splitkv", action="store_true",
+                    help="time attn_fwd_splitkv (default split count) instead of attn_fwd")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="with --splitkv: this split count instead of the default")
     ap.add_argument("--no-graph", action="store_true",
                     help="time K plain launches instead of one replay of a graph of K launches")
     ap.add_argument("--no-naive", action="store_true",
@@ -230,10 +234,21 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     scale = float(w.scale)
+    code = attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16
+    n_splits = None
+    if args.splitkv:
+        n_splits = args.kv_splits if args.kv_splits > 0 else \
+            attn.attn_fwd_splitkv_default_splits(code, w.B, w.H, w.N, w.d, w.causal)
+        ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, n_splits) // 4,
+                         dtype=torch.float32, device=dev)
 
     def step():
         # on the current stream (the capture stream while a graph records)
-        attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
+        if n_splits is not None:
+            attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits, scale=scale,
+                                  causal=w.causal, key_len=kl)
+        else:
+            attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
 
     # Untimed warmup: W steps, continued until at least --warmup-seconds of
     # GPU work has run, so that the clocks have left their idle state (the
@@ -280,8 +295,9 @@ def main():
     key_len = case["key_len"]
     pairs = visible_pairs(w, key_len)
     F_alg = 4.0 * w.d * pairs
-    kernel = attn.attn_fwd_kernel_name(attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16,
-                                       w.d, w.N, w.causal, key_len is not None)
+    kernel = attn.attn_fwd_kernel_name(code, w.d, w.N, w.causal, key_len is not None)
+    if n_splits is not None:
+        kernel = kernel.replace("attn_fwd_", "attn_fwd_split_", 1)
     if w.key_padding:
         nbytes = algorithmic_bytes(w, key_len)
         achieved = nbytes / launch_s / 1e9
@@ -301,11 +317,13 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
         "launch": "plain" if args.no_graph else "hip_graph",
+        "entry": "attn_fwd_splitkv" if n_splits is not None else "attn_fwd",
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "key_padding": w.key_padding, "seed": w.seed,
+                   "kv_splits": n_splits,
                    "global_batch": w.B, "seq_len": w.N},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
         "roofline": roof,

@@ -26,6 +26,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_MISALIGNED", 4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH",
           6: "ATTN_ERR_DEVICE"}
 EXPORTS = ["attn_fwd", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
+           "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_splitkv_default_splits",
            "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
 
 
@@ -48,6 +50,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_naive.restype = i32
     lib.attn_fwd_naive_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_fwd_naive_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_splitkv.argtypes = common + [i64, p, ctypes.c_size_t, p]
+    lib.attn_fwd_splitkv.restype = i32
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_splitkv_default_splits.argtypes = [i32, i64, i64, i64, i64, i32]
+    lib.attn_fwd_splitkv_default_splits.restype = i64
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_fwd_kernel_name.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, ctypes.c_size_t]
@@ -125,6 +133,29 @@ def attn_fwd_naive(q, k, v, o, lse=None, *, workspace: torch.Tensor, scale: floa
 
 def attn_fwd_naive_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(lib.attn_fwd_naive_workspace_bytes(B, H, N))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse=None, *, workspace: torch.Tensor, n_splits: int,
+                     scale: float, causal: bool = False, key_len=None, stream=None) -> None:
+    """Fused forward over ``n_splits`` key ranges, merged (see include/attn.h)."""
+    code = _dtype_code(q)
+    _check_tensors(q, k, v, o, lse, key_len)
+    B, H, N, d = q.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_splitkv(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              B, H, N, d, float(scale), int(bool(causal)), _ptr(key_len),
+                              int(n_splits), _ptr(workspace), nbytes, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_splitkv", st)
+
+
+def attn_fwd_splitkv_workspace_bytes(B: int, H: int, N: int, d: int, n_splits: int) -> int:
+    return int(lib.attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits))
+
+
+def attn_fwd_splitkv_default_splits(dtype: int, B: int, H: int, N: int, d: int,
+                                    causal: bool) -> int:
+    return int(lib.attn_fwd_splitkv_default_splits(dtype, B, H, N, d, int(bool(causal))))
 
 
 def attn_status_string(status: int) -> str:

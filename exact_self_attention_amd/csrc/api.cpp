@@ -18,6 +18,7 @@
 namespace {
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -104,6 +105,10 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void *Q, const void *K, const v
     p.BH = (int)(B * H);
     p.H = (int)H;
     p.n_qtiles = 0;
+    p.kv_splits = 1;
+    p.split_tiles = 0;
+    p.part_O = nullptr;
+    p.part_LSE = nullptr;
     // The kernel needs a positive exp2 scale (masked scores are -inf and must
     // map to exactly 0).  A zero scale becomes 1e-30: every score times it
     // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.
@@ -161,6 +166,88 @@ attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, c
             return ATTN_ERR_LAUNCH;
     }
     return ATTN_OK;
+}
+
+attn_status_t attn_fwd_splitkv(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                               void *O, float *LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                               float scale, int causal, const int32_t *key_len, int64_t n_splits,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    bool empty = false;
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    if (st != ATTN_OK) return st;
+    if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+    if (empty) return ATTN_OK;
+    const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits);
+    if (need == 0) return ATTN_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_MISALIGNED;
+    const size_t elems = (size_t)B * (size_t)H * (size_t)N;
+    if (overlaps(workspace, workspace_bytes, Q, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, K, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, V, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, O, elems * d * 2) ||
+        overlaps(workspace, workspace_bytes, LSE, LSE ? elems * 4 : 0) ||
+        overlaps(workspace, workspace_bytes, key_len, key_len ? (size_t)B * 4 : 0))
+        return ATTN_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != ATTN_OK) return st;
+
+    // whole 64-key tiles per split; trailing splits that would be empty for
+    // every row are not launched
+    const int64_t tiles = (N + 63) / 64;
+    const int64_t per = (tiles + n_splits - 1) / n_splits;
+    const int64_t used = (tiles + per - 1) / per;
+    attn::FwdParams p;
+    p.Q = static_cast<const uint16_t *>(Q);
+    p.K = static_cast<const uint16_t *>(K);
+    p.V = static_cast<const uint16_t *>(V);
+    p.O = static_cast<uint16_t *>(O);
+    p.LSE = LSE;
+    p.key_len = key_len;
+    p.N = N;
+    p.BH = (int)(B * H);
+    p.H = (int)H;
+    p.n_qtiles = 0;
+    p.kv_splits = (int)used;
+    p.split_tiles = (int)per;
+    p.part_O = static_cast<float *>(workspace);
+    p.part_LSE = p.part_O + (size_t)used * elems * (size_t)d;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
+    const hipError_t e = attn::launch_fwd_split(dtype == ATTN_BF16, (int)d, causal != 0, p,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+                                        int64_t n_splits) {
+    if (B < 0 || H < 0 || N < 0 || N > kMaxN || d < 0 || d > 1024 || n_splits < 1 ||
+        n_splits > kMaxSplits)
+        return 0;
+    const unsigned __int128 total = (unsigned __int128)n_splits * (unsigned __int128)B *
+                                    (unsigned __int128)H * (unsigned __int128)N *
+                                    (unsigned __int128)(d + 1) * 4u;
+    if (total > (unsigned __int128)SIZE_MAX) return 0;
+    return (size_t)total;
+}
+
+int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
+                                        int64_t d, int causal) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return 1;
+    if (d != 32 && d != 64 && d != 128) return 1;
+    if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN || H > INT32_MAX / B) return 1;
+    if (check_device() != ATTN_OK) return 1;
+    const int resident = attn::fwd_split_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0);
+    if (resident <= 0) return 1;
+    const int64_t rows = attn::fwd_query_rows_per_item();
+    const int64_t items = (N + rows - 1) / rows * B * H;
+    if (items >= resident) return 1;
+    const int64_t tiles = (N + 63) / 64;
+    int64_t s = (resident + items - 1) / items;
+    const int64_t max_s = tiles / 2 > 1 ? tiles / 2 : 1;
+    if (s > max_s) s = max_s;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : s;
 }
 
 size_t attn_fwd_naive_workspace_bytes(int64_t B, int64_t H, int64_t N) {

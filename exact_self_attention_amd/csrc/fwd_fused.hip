@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "cdna4.h"
@@ -112,7 +113,7 @@ __device__ __forceinline__ void sched_steps() {
     }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int TILE = kBN * D;                 // halves per K or V tile
@@ -135,8 +136,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int rb = 2 * simd + grp;   // this wave's 32-row block in the tile
 
     const int BH = p.BH;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
+    // workgroup -> (key split, query tile, head)
+    const int per_split = p.n_qtiles * BH;
+    const int sp = SPLIT ? (int)blockIdx.x / per_split : 0;
+    const int wg = (int)blockIdx.x - sp * per_split;
+    const int bh = wg % BH;
+    int qt = wg / BH;
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
     const int N = (int)p.N;
     const int b = bh / p.H;
@@ -153,12 +158,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int q0 = qt * kBM;
     int kv_end = Lk;
     if (CAUSAL) kv_end = min(kv_end, q0 + kBM);
-    const int n = (kv_end + kBN - 1) / kBN;       // key tiles of the workgroup
+    // key tiles j_begin .. j_begin + n - 1 (all visible tiles unless split)
+    const int n_all = (kv_end + kBN - 1) / kBN;
+    const int j_begin = SPLIT ? sp * p.split_tiles : 0;
+    const int n = SPLIT ? max(0, min(n_all - j_begin, p.split_tiles)) : n_all;
     const int qw0 = q0 + rb * kQRows;
     const int my_q = qw0 + l32;
     const bool q_ok = my_q < N;
     int n_w = n;                                  // key tiles this wave computes
-    if (CAUSAL) n_w = (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN;
+    if (CAUSAL) n_w = max(0, min(n, (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN - j_begin));
     if (qw0 >= N) n_w = 0;
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -215,7 +223,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // zeros to LDS without touching memory (and every batch has the same
     // number of instructions, which the waits below count on).
     auto tile_rsrc = [&](const uint16_t *src, int j) -> i32x4 {
-        const int j0 = j * kBN;
+        const int j0 = (j + j_begin) * kBN;
         const int rows = j < n ? min(kBN, Lk - j0) : 0;
         return make_rsrc(src + (size_t)(j < n ? j0 : 0) * D, (uint32_t)(rows * D * 2));
     };
@@ -328,7 +336,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     auto row_max = [&]() -> float { return row_max64(s); };
     auto exps = [&](float neg_m) -> float { return exps64<BF16>(s, c, neg_m, pf); };
     auto softmax = [&](int j) {
-        const int j0 = j * kBN;
+        const int j0 = (j + j_begin) * kBN;
         const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
         if (need_mask) {
 #pragma unroll
@@ -445,7 +453,26 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const Halves lh = both_halves(l_run);
     const float l_tot = lh.lo + lh.hi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (q_ok) {
+    if (SPLIT) {
+        // this split's normalised partial output and its LSE, in fp32; a row
+        // with no visible key in the split gets only LSE = -inf (the merge
+        // then ignores its output)
+        if (q_ok) {
+            const size_t row = ((size_t)sp * BH + bh) * (size_t)N + my_q;
+            float *orow = p.part_O + row * D;
+            if (l_tot > 0.f)
+#pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 w = {oacc[cb][4 * a] * inv, oacc[cb][4 * a + 1] * inv,
+                               oacc[cb][4 * a + 2] * inv, oacc[cb][4 * a + 3] * inv};
+                    *reinterpret_cast<f32x4 *>(orow + cb * 32 + a * 8 + g * 4) = w;
+                }
+            if (g == 0)
+                p.part_LSE[row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+    } else if (q_ok) {
         uint16_t *orow = p.O + base + (size_t)my_q * D;
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb)
@@ -466,7 +493,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
 
 #define ATTN_FWD_INSTANCE(NAME, D, BF16, CAUSAL)                                   \
     extern "C" __global__ __launch_bounds__(attn::kThreads)                       \
-    void NAME(attn::FwdParams p) { attn::fwd_body<D, BF16, CAUSAL>(p); }
+    void NAME(attn::FwdParams p) { attn::fwd_body<D, BF16, CAUSAL, false>(p); }
+#define ATTN_SPLIT_INSTANCE(NAME, D, BF16, CAUSAL)                                 \
+    extern "C" __global__ __launch_bounds__(attn::kThreads)                       \
+    void NAME(attn::FwdParams p) { attn::fwd_body<D, BF16, CAUSAL, true>(p); }
 
 ATTN_FWD_INSTANCE(attn_fwd_d32_f16_full, 32, false, false)
 ATTN_FWD_INSTANCE(attn_fwd_d32_f16_causal, 32, false, true)
@@ -480,6 +510,78 @@ ATTN_FWD_INSTANCE(attn_fwd_d128_f16_full, 128, false, false)
 ATTN_FWD_INSTANCE(attn_fwd_d128_f16_causal, 128, false, true)
 ATTN_FWD_INSTANCE(attn_fwd_d128_bf16_full, 128, true, false)
 ATTN_FWD_INSTANCE(attn_fwd_d128_bf16_causal, 128, true, true)
+
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d32_f16_full, 32, false, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d32_f16_causal, 32, false, true)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d32_bf16_full, 32, true, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d32_bf16_causal, 32, true, true)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d64_f16_full, 64, false, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d64_f16_causal, 64, false, true)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d64_bf16_full, 64, true, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d64_bf16_causal, 64, true, true)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d128_f16_full, 128, false, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d128_f16_causal, 128, false, true)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d128_bf16_full, 128, true, false)
+ATTN_SPLIT_INSTANCE(attn_fwd_split_d128_bf16_causal, 128, true, true)
+
+namespace attn {
+namespace {
+
+// Merge of the key-range splits of every row, one thread per 4 output
+// columns: LSE = m + log sum_s exp(LSE_s - m) with m = max_s LSE_s, and
+// O = sum_s exp(LSE_s - m) O_s / sum_s exp(LSE_s - m), which is the
+// online-softmax merge of "Self-Attention Kernel & Inference Engine from
+// Scratch" ("Online Softmax Formulation") applied to whole blocks.  Rows
+// whose splits are all empty get O = 0 and LSE = -inf.
+struct MergeParams {
+    const float *part_O;
+    const float *part_LSE;
+    uint16_t *O;
+    float *LSE;
+    int64_t rows;  // B * H * N
+    int d;
+    int splits;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void merge_body(const MergeParams &p) {
+    const int chunks = p.d / 4;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t / chunks;
+    const int c = (int)(t - row * chunks);
+    if (row >= p.rows) return;
+    float m = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_LSE[(int64_t)s * p.rows + row]);
+    uint16_t *orow = p.O + row * p.d + 4 * c;
+    if (m == -INFINITY) {
+        *reinterpret_cast<u32x2 *>(orow) = (u32x2){0u, 0u};
+        if (p.LSE != nullptr && c == 0) p.LSE[row] = -INFINITY;
+        return;
+    }
+    float wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) {
+        const float l = p.part_LSE[(int64_t)s * p.rows + row];
+        if (l == -INFINITY) continue;  // an empty split (its O_s is 0)
+        const float w = fast_exp2((l - m) * 1.44269504088896341f);
+        wsum += w;
+        acc += w * *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c);
+    }
+    const float inv = 1.f / wsum;
+    *reinterpret_cast<u32x2 *>(orow) =
+        (u32x2){pack2<BF16>(acc[0] * inv, acc[1] * inv), pack2<BF16>(acc[2] * inv, acc[3] * inv)};
+    if (p.LSE != nullptr && c == 0) p.LSE[row] = m + __builtin_logf(wsum);
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" __global__ __launch_bounds__(256) void attn_fwd_split_merge_f16(attn::MergeParams p) {
+    attn::merge_body<false>(p);
+}
+extern "C" __global__ __launch_bounds__(256) void attn_fwd_split_merge_bf16(attn::MergeParams p) {
+    attn::merge_body<true>(p);
+}
 
 namespace attn {
 
@@ -499,12 +601,22 @@ const FwdEntry kFwdTable[12] = {
     ATTN_ENTRY(attn_fwd_d128_f16_full),  ATTN_ENTRY(attn_fwd_d128_f16_causal),
     ATTN_ENTRY(attn_fwd_d128_bf16_full), ATTN_ENTRY(attn_fwd_d128_bf16_causal),
 };
+const FwdEntry kSplitTable[12] = {
+    ATTN_ENTRY(attn_fwd_split_d32_f16_full),   ATTN_ENTRY(attn_fwd_split_d32_f16_causal),
+    ATTN_ENTRY(attn_fwd_split_d32_bf16_full),  ATTN_ENTRY(attn_fwd_split_d32_bf16_causal),
+    ATTN_ENTRY(attn_fwd_split_d64_f16_full),   ATTN_ENTRY(attn_fwd_split_d64_f16_causal),
+    ATTN_ENTRY(attn_fwd_split_d64_bf16_full),  ATTN_ENTRY(attn_fwd_split_d64_bf16_causal),
+    ATTN_ENTRY(attn_fwd_split_d128_f16_full),  ATTN_ENTRY(attn_fwd_split_d128_f16_causal),
+    ATTN_ENTRY(attn_fwd_split_d128_bf16_full), ATTN_ENTRY(attn_fwd_split_d128_bf16_causal),
+};
+
 #undef ATTN_ENTRY
 
 int d_index(int d) { return d == 32 ? 0 : (d == 64 ? 1 : 2); }
-const FwdEntry &entry(bool bf16, int d, bool causal) {
-    return kFwdTable[(d_index(d) * 2 + (bf16 ? 1 : 0)) * 2 + (causal ? 1 : 0)];
+int table_index(bool bf16, int d, bool causal) {
+    return (d_index(d) * 2 + (bf16 ? 1 : 0)) * 2 + (causal ? 1 : 0);
 }
+const FwdEntry &entry(bool bf16, int d, bool causal) { return kFwdTable[table_index(bf16, d, causal)]; }
 }  // namespace
 
 const char *fwd_fused_kernel_name(bool bf16, int d, bool causal) {
@@ -517,6 +629,58 @@ hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStrea
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(entry(bf16, d, causal).fn, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+int fwd_query_rows_per_item() { return kBM; }
+
+const char *fwd_split_kernel_name(bool bf16, int d, bool causal) {
+    return kSplitTable[table_index(bf16, d, causal)].name;
+}
+
+int fwd_split_resident_workgroups(bool bf16, int d, bool causal) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices][12];
+    const int index = table_index(bf16, d, causal);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = cache[dev][index].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(kSplitTable[index].fn), kThreads, 0) != hipSuccess)
+        return 0;
+    const int r = cus * (per_cu > 0 ? per_cu : 1);
+    if (dev < kMaxDevices) cache[dev][index].store(r, std::memory_order_relaxed);
+    return r;
+}
+
+hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
+    p.n_qtiles = (int)((p.N + kBM - 1) / kBM);
+    const int64_t blocks = (int64_t)p.n_qtiles * p.BH * p.kv_splits;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL || p.kv_splits < 1 || p.split_tiles < 1)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kSplitTable[table_index(bf16, d, causal)].fn, dim3((unsigned)blocks),
+                       dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MergeParams m;
+    m.part_O = p.part_O;
+    m.part_LSE = p.part_LSE;
+    m.O = p.O;
+    m.LSE = p.LSE;
+    m.rows = (int64_t)p.BH * p.N;
+    m.d = d;
+    m.splits = p.kv_splits;
+    const int64_t threads = m.rows * (d / 4);
+    const int64_t mblocks = (threads + 255) / 256;
+    if (mblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bf16 ? attn_fwd_split_merge_bf16 : attn_fwd_split_merge_f16,
+                       dim3((unsigned)mblocks), dim3(256), 0, s, m);
     return hipGetLastError();
 }
 

@@ -20,6 +20,13 @@ struct FwdParams {
     int H;
     int n_qtiles;               // ceil(N / query rows per workgroup)
     float scale_log2;           // scale * log2(e), > 0
+    // Key-range split (attn_fwd_splitkv): workgroup slice s covers key tiles
+    // [s * split_tiles, (s + 1) * split_tiles) and writes its normalised
+    // partial output and LSE, in fp32, to part_O / part_LSE.
+    int kv_splits;              // 1: no split
+    int split_tiles;            // 64-key tiles per split
+    float *part_O;              // [kv_splits][B*H][N][d]
+    float *part_LSE;            // [kv_splits][B*H][N]
 };
 
 // Streaming kernel (any N): 8 waves, 256 query rows per workgroup, K/V
@@ -27,6 +34,15 @@ struct FwdParams {
 // between two wave groups.  p.n_qtiles is filled in here.
 hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
 const char *fwd_fused_kernel_name(bool bf16, int d, bool causal);
+
+// Split-key forward: the streaming kernel over p.kv_splits key ranges into
+// p.part_O / p.part_LSE, then a merge of the partial results into O and LSE
+// (LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s).
+hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
+const char *fwd_split_kernel_name(bool bf16, int d, bool causal);
+// Workgroups of the split kernel the current device holds at once (0 on error).
+int fwd_split_resident_workgroups(bool bf16, int d, bool causal);
+int fwd_query_rows_per_item();
 
 // Short-sequence kernel (N <= fwd_short_max_keys(d)): 4 waves, 128 query
 // rows per workgroup, the head's whole K and V resident in LDS.

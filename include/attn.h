@@ -122,6 +122,48 @@ attn_status_t attn_fwd_naive(attn_dtype_t dtype,
  * B * H * N * N * 4.  Returns 0 for negative sizes or on overflow. */
 size_t attn_fwd_naive_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
+/*
+ * attn_fwd_splitkv -- the fused forward with each row's key range cut into
+ * splits, for shapes whose (b, h, 256-row query tile) work items are too
+ * few to occupy the GPU (few heads, long sequences).
+ *
+ * The visible keys of every row are divided into up to n_splits ranges of
+ * whole 64-key tiles; workgroups compute each range as attn_fwd does and
+ * write its normalised partial output O_s and log-sum-exp LSE_s (fp32) to
+ * the workspace; a second launch merges them per row with the identity of
+ * "Self-Attention Kernel & Inference Engine from Scratch" ("Online Softmax
+ * Formulation") applied to whole blocks: LSE = log sum_s exp(LSE_s) and
+ * O = sum_s exp(LSE_s - LSE) O_s.  The result equals attn_fwd's up to
+ * rounding (O is rounded to dtype once, after the merge).
+ *
+ * Arguments as attn_fwd, plus: n_splits >= 1 (at most 4096; splits beyond
+ * the key tiles a row has are empty and cost nothing); workspace: device
+ * memory of at least attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits)
+ * bytes, 16-byte aligned, owned by the caller, overwritten, and overlapping
+ * no tensor.  Returns ATTN_ERR_WORKSPACE when it is NULL or too small,
+ * ATTN_ERR_INVALID_ARG for n_splits out of range or an overlap, otherwise
+ * as attn_fwd.  Two launches on stream, asynchronous.
+ */
+attn_status_t attn_fwd_splitkv(attn_dtype_t dtype,
+                               const void *Q, const void *K, const void *V,
+                               void *O, float *LSE,
+                               int64_t B, int64_t H, int64_t N, int64_t d,
+                               float scale, int causal, const int32_t *key_len,
+                               int64_t n_splits, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * N * (d + 1) * 4.
+ * Returns 0 for sizes out of range or on overflow. */
+size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+                                        int64_t n_splits);
+
+/* A split count that lets the work items of (dtype, B, H, N, d, causal)
+ * occupy every compute unit of the current device: 1 when the unsplit
+ * kernel already does, else enough splits to fill the resident workgroups,
+ * keeping at least two key tiles per split.  Returns 1 on any error. */
+int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
+                                        int64_t d, int causal);
+
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(attn_status_t status);
 

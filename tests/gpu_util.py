@@ -76,6 +76,25 @@ def run_naive(case: dict, causal: bool, inputs=None, max_workspace_bytes=None):
     return from_dev(o, case["dtype"]), lse.cpu().numpy()
 
 
+def run_split(case: dict, causal: bool, n_splits=None, inputs=None):
+    """attn_fwd_splitkv with n_splits key ranges (None: the library's default)."""
+    import exact_self_attention_amd as attn
+    q, k, v, kl = inputs if inputs is not None else dev_inputs(case)
+    B, H, N, d = q.shape
+    if n_splits is None:
+        code = attn.ATTN_F16 if case["dtype"] == "f16" else attn.ATTN_BF16
+        n_splits = attn.attn_fwd_splitkv_default_splits(code, B, H, N, d, causal)
+    nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits)
+    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
+                          scale=float(case["scale"]), causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    del ws
+    return from_dev(o, case["dtype"]), lse.cpu().numpy(), n_splits
+
+
 def oracle_rows(case: dict, causal: bool, sel: np.ndarray):
     dt = case["dtype"]
     Q = ai.bits_to_f32(case["Q"], dt)

@@ -134,3 +134,42 @@ def test_python_layer_checks_tensors(lib):
         lib.attn_fwd(q, q, q, q.clone(), scale=0.1)
     with pytest.raises(TypeError):
         lib.attn_fwd(q.float(), q.float(), q.float(), q.float(), scale=0.1)
+
+
+def call_split(lib, n_splits=2, ws=A + 256 * MB, ws_bytes=None, **kw):
+    a = dict(dtype=0, Q=A, K=A + 64 * MB, V=A + 128 * MB, O=A + 192 * MB, LSE=None,
+             B=1, H=2, N=64, d=64, scale=0.125, causal=0, key_len=None)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_fwd_splitkv_workspace_bytes(a["B"], a["H"], a["N"], a["d"], max(n_splits, 1))
+    return lib.lib.attn_fwd_splitkv(a["dtype"], a["Q"], a["K"], a["V"], a["O"], a["LSE"],
+                                    a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                                    a["key_len"], n_splits, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_bytes(lib):
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 4, 4096, 128, 4) == 4 * 1 * 4 * 4096 * 129 * 4
+    assert lib.attn_fwd_splitkv_workspace_bytes(2, 3, 100, 32, 1) == 2 * 3 * 100 * 33 * 4
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 64, 64, 0) == 0        # no splits
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 64, 64, 4097) == 0     # too many
+    assert lib.attn_fwd_splitkv_workspace_bytes(-1, 1, 64, 64, 2) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(1 << 20, 1 << 20, 1 << 20, 128, 8) == 0  # overflow
+
+
+def test_splitkv_argument_checks(lib):
+    assert call_split(lib, n_splits=0) == INVALID
+    assert call_split(lib, n_splits=5000) == INVALID
+    assert call_split(lib, ws=None) == WORKSPACE
+    need = lib.attn_fwd_splitkv_workspace_bytes(1, 2, 64, 64, 2)
+    assert call_split(lib, ws_bytes=need - 1) == WORKSPACE
+    assert call_split(lib, ws=A + 256 * MB + 8) == MISALIGNED
+    assert call_split(lib, ws=A + 192 * MB) == INVALID       # workspace overlaps O
+    assert call_split(lib, d=48) == UNSUPPORTED
+    assert call_split(lib, scale=-1.0) == INVALID
+    assert call_split(lib, B=0, ws=None, ws_bytes=0) == 0   # empty problem: no-op
+
+
+def test_splitkv_default_splits_without_device(lib):
+    # no usable device here (or a bad argument): the default is 1 split
+    assert lib.attn_fwd_splitkv_default_splits(0, 1, 4, 4096, 128, False) >= 1
+    assert lib.attn_fwd_splitkv_default_splits(0, 1, 4, 4096, 48, False) == 1

@@ -216,3 +216,60 @@ def test_streaming_many_items_per_workgroup(B, H, N, d, causal, dtype):
     O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
     Og, Lg = gu.gather(O, LSE, sel)
     gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"stream B={B} H={H} N={N} d={d} causal={causal}", sel)
+
+
+# attn_fwd_splitkv: key ranges computed by separate workgroups and merged.
+# Cases cover every d, both dtypes, causal, key lengths 0 / 1 / short / full,
+# one split, and more splits than a row has key tiles (empty splits).
+SPLIT_CASES = [
+    # (B, H, N, d, causal, dtype, n_splits)
+    (4, 3, 1000, 128, False, ai.F16, 3),
+    (4, 3, 1000, 128, True, ai.BF16, 4),
+    (4, 3, 700, 64, False, ai.BF16, 5),
+    (4, 3, 700, 64, True, ai.F16, 2),
+    (4, 2, 300, 32, False, ai.F16, 3),
+    (4, 2, 513, 128, True, ai.F16, 64),
+    (4, 2, 200, 64, False, ai.BF16, 1),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dtype,S", SPLIT_CASES,
+                         ids=[f"B{b}H{h}N{n}d{d}{'c' if c else 'f'}{t}S{s}" for b, h, n, d, c, t, s in SPLIT_CASES])
+def test_splitkv_matches_oracle(B, H, N, d, causal, dtype, S):
+    seed = 30_000 + B + H + N + d + causal + S
+    kl = [N, 1, 0, int(np.random.default_rng(seed).integers(2, N + 1))]
+    case = ai.random_case(B, H, N, d, dtype, seed=seed, sigma=1.5, key_len=kl)
+    gu.log(f"splitkv B={B} H={H} N={N} d={d} causal={causal} {dtype} S={S} key_len={kl}")
+    O, LSE, _ = gu.run_split(case, causal, S)
+    sel = ai.all_rows_selection(B, H, N)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"splitkv N={N} d={d} S={S}", sel)
+
+
+def test_splitkv_default_splits_long_few_heads():
+    # few heads, long causal sequence: the default split count fills the GPU
+    B, H, N, d = 1, 4, 8192, 128
+    case = ai.random_case(B, H, N, d, ai.BF16, seed=31_001, sigma=1.0)
+    O, LSE, S = gu.run_split(case, True)
+    gu.log(f"splitkv default splits for B={B} H={H} N={N}: {S}")
+    assert S > 1
+    sel = gu.sample_rows(B, H, N, 48, seed=31_002)
+    O_ref, LSE_ref = gu.oracle_rows(case, True, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, ai.BF16, "splitkv default S", sel)
+
+
+def test_prefill_shard_workload_fused_and_split():
+    # the prefill's 8-way head shard: both entry points on the workload's inputs
+    w = ai.WORKLOADS["prefill_shard8"]
+    case = ai.generate(w)
+    sel = gu.sample_rows(w.B, w.H, w.N, 64, seed=w.seed + 7)
+    O_ref, LSE_ref = gu.oracle_rows(case, w.causal, sel)
+    O, LSE = gu.run_fused(case, w.causal)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, "prefill_shard8 fused", sel)
+    O, LSE, S = gu.run_split(case, w.causal)
+    gu.log(f"prefill_shard8 default splits: {S}")
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"prefill_shard8 split S={S}", sel)
