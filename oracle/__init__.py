@@ -30,7 +30,7 @@ _lib = None
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle with gcc into ``out`` (always recompiles)."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.{os.getpid()}.tmp"
     subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, out)
     return out
@@ -45,9 +45,9 @@ def load(path: str = _LIB, *, build_if_missing: bool = True) -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
-    lib.oracle_sdpa_rows.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double,
+    lib.oracle_attn_rows.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_double,
                                      ctypes.c_int, p, p, i64, p, p]
-    lib.oracle_sdpa_rows.restype = ctypes.c_int
+    lib.oracle_attn_rows.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -68,20 +68,25 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def sdpa_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
-    """Oracle attention on selected rows.
+def attn_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
+    """Oracle attention on selected rows, general shapes.
 
-    Q, K, V: float32 ``[B, H, N, d]``; ``key_len``: int ``[B]`` or None;
-    ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE ``[n]``)
-    in float64.
+    Q: float32 ``[B, H, Nq, d]``; K, V: float32 ``[B, Hkv, Nk, d]`` with H a
+    multiple of Hkv (query head h reads key/value head h // (H // Hkv));
+    causal visibility is j <= i + Nk - Nq.  ``key_len``: int ``[B]`` or None;
+    ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE
+    ``[n]``) in float64.
     """
     lib = lib or _get()
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     K = np.ascontiguousarray(K, dtype=np.float32)
     V = np.ascontiguousarray(V, dtype=np.float32)
-    if Q.ndim != 4 or K.shape != Q.shape or V.shape != Q.shape:
-        raise ValueError("Q, K, V must share one [B, H, N, d] shape")
-    B, H, N, d = Q.shape
+    if Q.ndim != 4 or K.ndim != 4 or V.shape != K.shape:
+        raise ValueError("Q must be [B, H, Nq, d] and K, V one [B, Hkv, Nk, d] shape")
+    B, H, Nq, d = Q.shape
+    Bk, Hkv, Nk, dk = K.shape
+    if Bk != B or dk != d or Hkv == 0 or H % Hkv != 0:
+        raise ValueError("K/V batch and head size must match Q, and Hkv divide H")
     sel = np.ascontiguousarray(sel, dtype=np.int64).reshape(-1, 3)
     n = sel.shape[0]
     O = np.zeros((n, d), dtype=np.float64)
@@ -91,20 +96,42 @@ def sdpa_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
         kl = np.ascontiguousarray(key_len, dtype=np.int32)
         if kl.shape != (B,):
             raise ValueError("key_len must have shape [B]")
-    rc = lib.oracle_sdpa_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d,
+    rc = lib.oracle_attn_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, Hkv, Nq, Nk, d,
                               float(scale), int(bool(causal)),
                               None if kl is None else _ptr(kl),
                               _ptr(sel), n, _ptr(O), _ptr(LSE))
     if rc != 0:
-        raise ValueError("oracle_sdpa_rows rejected its arguments")
+        raise ValueError("oracle_attn_rows rejected its arguments")
     return O, LSE
 
 
-def sdpa(Q, K, V, scale, causal: bool = False, key_len=None, *, lib=None):
-    """Oracle attention on every row: O ``[B,H,N,d]`` and LSE ``[B,H,N]`` (float64)."""
+def attn(Q, K, V, scale, causal: bool = False, key_len=None, *, lib=None):
+    """Oracle attention on every row, general shapes: O ``[B,H,Nq,d]`` and
+    LSE ``[B,H,Nq]`` (float64)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
-    B, H, N, d = Q.shape
-    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    B, H, Nq, d = Q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(Nq), indexing="ij")
     sel = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
-    O, LSE = sdpa_rows(Q, K, V, scale, causal, key_len, sel, lib=lib)
-    return O.reshape(B, H, N, d), LSE.reshape(B, H, N)
+    O, LSE = attn_rows(Q, K, V, scale, causal, key_len, sel, lib=lib)
+    return O.reshape(B, H, Nq, d), LSE.reshape(B, H, Nq)
+
+
+def sdpa_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
+    """Oracle self-attention on selected rows.
+
+    Q, K, V: float32 ``[B, H, N, d]``; ``key_len``: int ``[B]`` or None;
+    ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE ``[n]``)
+    in float64.
+    """
+    Q = np.asarray(Q)
+    if Q.ndim != 4 or np.shape(K) != Q.shape or np.shape(V) != Q.shape:
+        raise ValueError("Q, K, V must share one [B, H, N, d] shape")
+    return attn_rows(Q, K, V, scale, causal, key_len, sel, lib=lib)
+
+
+def sdpa(Q, K, V, scale, causal: bool = False, key_len=None, *, lib=None):
+    """Oracle self-attention on every row: O ``[B,H,N,d]`` and LSE ``[B,H,N]`` (float64)."""
+    Q = np.asarray(Q)
+    if Q.ndim != 4 or np.shape(K) != Q.shape or np.shape(V) != Q.shape:
+        raise ValueError("Q, K, V must share one [B, H, N, d] shape")
+    return attn(Q, K, V, scale, causal, key_len, lib=lib)

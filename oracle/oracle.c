@@ -21,12 +21,21 @@
  * (section 1, "Standard Attention: Step by Step") where the mask is
  * structural: a masked key gets probability exactly zero.
  *
+ * Shapes: Q and O are [B, H, Nq, d]; K and V are [B, Hkv, Nk, d] with H a
+ * multiple of Hkv.  Self-attention is Hkv = H and Nq = Nk.  Different
+ * query and key lengths (cross-attention) and fewer key/value heads than
+ * query heads (grouped-query attention) are the extensions the
+ * "cuda-reranker" page lists as future work; it does not define them, so
+ * this oracle fixes the usual reading: query head h reads key/value head
+ * floor(h / (H / Hkv)), i.e. consecutive query heads share one.
+ *
  * Visible keys (the readings this oracle fixes where the pages are silent):
- *   - key j is visible iff j < L_b, where L_b = clamp(key_len[b], 0, N) when a
- *     key-length array is given (a key-side padding mask, "cuda-reranker"),
- *     else L_b = N;
- *   - with causal masking additionally j <= i (top-left alignment, equal query
- *     and key lengths);
+ *   - key j is visible iff j < L_b, where L_b = clamp(key_len[b], 0, Nk) when
+ *     a key-length array is given (a key-side padding mask, "cuda-reranker"),
+ *     else L_b = Nk;
+ *   - with causal masking additionally j <= i + (Nk - Nq): the query rows
+ *     are aligned with the last Nq keys (bottom-right), which is j <= i
+ *     (top-left) when Nq = Nk;
  *   - a row with no visible key has O_i = 0 and LSE_i = -inf.
  *
  * The score row is materialised in full (one row at a time), followed by two
@@ -53,29 +62,32 @@ int oracle_max_threads(void) {
 }
 
 /*
- * Q, K, V: [B, H, N, d] row-major float32.
+ * Q: [B, H, Nq, d]; K, V: [B, Hkv, Nk, d]; all row-major float32.
  * key_len: [B] or NULL.
- * sel: n_sel triples (b, h, i) as int64.
+ * sel: n_sel triples (b, h, i) as int64, h a query head, i a query row.
  * O: [n_sel, d] double; LSE: [n_sel] double.
  * Returns 0, or -1 on a bad argument or a failed allocation.
  */
-int oracle_sdpa_rows(const float *Q, const float *K, const float *V,
-                     int64_t B, int64_t H, int64_t N, int64_t d,
+int oracle_attn_rows(const float *Q, const float *K, const float *V,
+                     int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                      double scale, int causal, const int32_t *key_len,
                      const int64_t *sel, int64_t n_sel,
                      double *O, double *LSE)
 {
-    if (B < 0 || H < 0 || N < 0 || d <= 0 || n_sel < 0) return -1;
+    if (B < 0 || H < 0 || Hkv <= 0 || H % Hkv != 0 || Nq < 0 || Nk < 0 || d <= 0 ||
+        n_sel < 0)
+        return -1;
     for (int64_t t = 0; t < n_sel; ++t) {
         int64_t b = sel[3 * t], h = sel[3 * t + 1], i = sel[3 * t + 2];
-        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return -1;
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Nq) return -1;
     }
+    const int64_t group = H / Hkv;   /* query heads per key/value head */
     int failed = 0;
 
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-        double *p = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *p = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
         if (s == NULL || p == NULL) {
 #pragma omp atomic write
             failed = 1;
@@ -84,20 +96,23 @@ int oracle_sdpa_rows(const float *Q, const float *K, const float *V,
         for (int64_t t = 0; t < n_sel; ++t) {
             if (s == NULL || p == NULL) continue;
             int64_t b = sel[3 * t], h = sel[3 * t + 1], i = sel[3 * t + 2];
-            const float *q  = Q + ((b * H + h) * N + i) * d;
-            const float *kb = K + (b * H + h) * N * d;
-            const float *vb = V + (b * H + h) * N * d;
+            int64_t hk = h / group;  /* the key/value head query head h reads */
+            const float *q  = Q + ((b * H + h) * Nq + i) * d;
+            const float *kb = K + (b * Hkv + hk) * Nk * d;
+            const float *vb = V + (b * Hkv + hk) * Nk * d;
             double *o = O + t * d;
 
             /* visible keys are j < n_vis */
-            int64_t L = N;
+            int64_t L = Nk;
             if (key_len != NULL) {
                 L = key_len[b];
                 if (L < 0) L = 0;
-                if (L > N) L = N;
+                if (L > Nk) L = Nk;
             }
             int64_t n_vis = L;
-            if (causal && i + 1 < n_vis) n_vis = i + 1;
+            /* causal: query row i sits at key position i + Nk - Nq */
+            int64_t pos = i + (Nk - Nq);
+            if (causal && pos + 1 < n_vis) n_vis = pos + 1 > 0 ? pos + 1 : 0;
 
             if (n_vis == 0) {
                 for (int64_t c = 0; c < d; ++c) o[c] = 0.0;

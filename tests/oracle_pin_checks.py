@@ -315,21 +315,30 @@ def check_weighted_average(lib):
 
 # ------------------------------------------------------------ library restatement
 def textbook_numpy(Q, K, V, scale, causal=False, key_len=None):
-    """softmax(scale Q K^T + mask) V with numpy matmul/exp/sum on float64 copies;
-    the mask is -inf above the diagonal (causal) and at keys j >= key_len[b]."""
+    """softmax(scale Q K^T + mask) V with numpy matmul/exp/sum on float64 copies.
+
+    Q is [B, H, Nq, d], K and V [B, Hkv, Nk, d]: the key/value heads are
+    expanded with np.repeat (consecutive query heads share one).  The mask
+    is -inf above the diagonal that ends at the last query and key
+    (np.tril with offset Nk - Nq; the plain lower triangle when Nq = Nk) and
+    at keys j >= key_len[b]."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
-    B, H, N, d = Q.shape
+    B, H, Nq, d = Q.shape
+    G = H // K.shape[1]
+    K = np.repeat(K, G, axis=1)
+    V = np.repeat(V, G, axis=1)
+    Nk = K.shape[2]
     S = scale * np.matmul(Q, np.swapaxes(K, -1, -2))
-    mask = np.zeros((B, 1, N, N))
+    mask = np.zeros((B, 1, Nq, Nk))
     if causal:
-        mask = mask + np.where(np.tril(np.ones((N, N))) > 0, 0.0, -np.inf)
+        mask = mask + np.where(np.tril(np.ones((Nq, Nk)), k=Nk - Nq) > 0, 0.0, -np.inf)
     if key_len is not None:
-        cols = np.arange(N)[None, :]
-        kl = np.clip(np.asarray(key_len), 0, N)[:, None]
+        cols = np.arange(Nk)[None, :]
+        kl = np.clip(np.asarray(key_len), 0, Nk)[:, None]
         mask = mask + np.where(cols < kl, 0.0, -np.inf)[:, None, None, :]
     S = S + mask
     with np.errstate(invalid="ignore"):
-        m = S.max(axis=-1, keepdims=True)
+        m = S.max(axis=-1, keepdims=True) if Nk > 0 else np.full((B, H, Nq, 1), -np.inf)
         E = np.exp(S - m)
         l = E.sum(axis=-1, keepdims=True)
         P = E / l
@@ -379,6 +388,89 @@ def check_online_merge_matches(lib):
                 m, l, o = summ[0]
                 assert np.allclose(o, O[0, h, i], rtol=1e-12, atol=1e-12)
                 assert abs(om.lse(summ[0]) - LSE[0, h, i]) < 1e-12
+
+
+# ------------------------------------------------------------ cross-attention and grouped heads
+def _run_general(lib, Q, K, V, scale, causal=False, key_len=None):
+    Q = np.asarray(Q, dtype=np.float32)
+    K = np.asarray(K, dtype=np.float32)
+    V = np.asarray(V, dtype=np.float32)
+    return oracle.attn(Q, K, V, scale, causal, key_len, lib=lib)
+
+
+def check_grouped_heads_equal_repeated_heads(lib):
+    """Hkv < H equals self-attention shapes with each key/value head copied to
+    the H / Hkv consecutive query heads that share it (np.repeat)."""
+    rng = _rng(31)
+    B, H, Hkv, N, d = 2, 6, 2, 23, 16
+    Q = _randn(rng, (B, H, N, d), 1.5)
+    K = _randn(rng, (B, Hkv, N, d), 1.5)
+    V = _randn(rng, (B, Hkv, N, d))
+    Kr, Vr = np.repeat(K, H // Hkv, axis=1), np.repeat(V, H // Hkv, axis=1)
+    for causal, kl in ((False, None), (True, np.array([23, 11], np.int32))):
+        O, LSE = _run_general(lib, Q, K, V, 0.3, causal, kl)
+        Or, LSEr = _run(lib, Q, Kr, Vr, 0.3, causal, kl)
+        assert np.array_equal(O, Or) and np.array_equal(LSE, LSEr)
+
+
+def check_cross_textbook_numpy(lib):
+    """Different query and key lengths and grouped heads against numpy."""
+    rng = _rng(32)
+    for (B, H, Hkv, Nq, Nk, d, causal, kl) in [
+            (1, 4, 1, 3, 17, 8, True, None), (2, 4, 2, 19, 7, 16, True, None),
+            (2, 3, 3, 5, 40, 32, False, [0, 33]), (1, 8, 2, 11, 29, 8, True, [20]),
+            (2, 2, 1, 1, 64, 16, True, [64, 9])]:
+        Q = _randn(rng, (B, H, Nq, d), 1.7)
+        K = _randn(rng, (B, Hkv, Nk, d), 1.7)
+        V = _randn(rng, (B, Hkv, Nk, d))
+        key_len = None if kl is None else np.array(kl, np.int32)
+        O, LSE = _run_general(lib, Q, K, V, 0.37, causal, key_len)
+        Oref, LSEref = textbook_numpy(Q, K, V, 0.37, causal, key_len)
+        assert np.allclose(O, Oref, rtol=1e-12, atol=1e-12)
+        fin = np.isfinite(LSEref)
+        assert np.array_equal(fin, np.isfinite(LSE))
+        assert np.allclose(LSE[fin], LSEref[fin], rtol=1e-12, atol=1e-12)
+
+
+def check_causal_queries_are_the_last_rows(lib):
+    """Bottom-right alignment: causal attention of the last Nq query rows
+    against all Nk keys equals rows Nk-Nq .. Nk-1 of causal self-attention
+    over the Nk rows; a single query row sees every key."""
+    rng = _rng(33)
+    B, H, N, d = 2, 2, 30, 8
+    Q, K, V = (_randn(rng, (B, H, N, d)) for _ in range(3))
+    O_self, LSE_self = _run(lib, Q, K, V, 0.45, causal=True)
+    for nq in (1, 4, 13):
+        O, LSE = _run_general(lib, Q[:, :, N - nq:], K, V, 0.45, causal=True)
+        assert np.array_equal(O, O_self[:, :, N - nq:])
+        assert np.array_equal(LSE, LSE_self[:, :, N - nq:])
+    O1, LSE1 = _run_general(lib, Q[:, :, :1], K, V, 0.45, causal=True)
+    O2, LSE2 = _run_general(lib, Q[:, :, :1], K, V, 0.45, causal=False)
+    assert np.array_equal(O1, O2) and np.array_equal(LSE1, LSE2)
+
+
+def check_cross_zero_query_prefix_means(lib):
+    """Q = 0 with Nq != Nk: query i averages the value rows up to key
+    i + Nk - Nq (causal), or all of them; more queries than keys leaves the
+    first Nq - Nk rows empty (O = 0, LSE = -inf)."""
+    rng = _rng(34)
+    for Nq, Nk in ((5, 12), (12, 5)):
+        B, H, Hkv, d = 1, 4, 2, 8
+        Q = np.zeros((B, H, Nq, d), np.float32)
+        K = _randn(rng, (B, Hkv, Nk, d))
+        V = _randn(rng, (B, Hkv, Nk, d))
+        for causal in (False, True):
+            O, LSE = _run_general(lib, Q, K, V, 1.0, causal)
+            for h in range(H):
+                hk = h // (H // Hkv)
+                for i in range(Nq):
+                    n = min(Nk, i + Nk - Nq + 1) if causal else Nk
+                    if n <= 0:
+                        assert np.all(O[0, h, i] == 0.0) and np.isneginf(LSE[0, h, i])
+                        continue
+                    ref = V[0, hk, :n].astype(np.float64).mean(axis=0)
+                    assert np.allclose(O[0, h, i], ref, rtol=0, atol=1e-14)
+                    assert abs(LSE[0, h, i] - math.log(n)) < 1e-14
 
 
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -19,10 +19,15 @@ MUTANTS = {
     "exp_sign_flipped": ("p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
     "exp2_for_exp": ("p[j] = exp(s[j] - m);", "p[j] = exp2(s[j] - m);"),
     "no_normalisation": ("for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;", ""),
-    "causal_strict": ("if (causal && i + 1 < n_vis) n_vis = i + 1;",
-                      "if (causal && i < n_vis) n_vis = i;"),
-    "causal_ignored": ("if (causal && i + 1 < n_vis) n_vis = i + 1;", ""),
-    "key_len_ignored": ("L = key_len[b];", "L = N;"),
+    "causal_strict": ("if (causal && pos + 1 < n_vis) n_vis = pos + 1 > 0 ? pos + 1 : 0;",
+                      "if (causal && pos < n_vis) n_vis = pos > 0 ? pos : 0;"),
+    "causal_ignored": ("if (causal && pos + 1 < n_vis) n_vis = pos + 1 > 0 ? pos + 1 : 0;", ""),
+    "causal_top_left": ("int64_t pos = i + (Nk - Nq);", "int64_t pos = i;"),
+    "causal_offset_sign": ("int64_t pos = i + (Nk - Nq);", "int64_t pos = i + (Nq - Nk);"),
+    "kv_head_interleaved": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
+    "query_head_from_kv_head": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
+                                "const float *q  = Q + ((b * H + hk) * Nq + i) * d;"),
+    "key_len_ignored": ("L = key_len[b];", "L = Nk;"),
     "key_operand_for_query": ("dot += (double)q[c] * (double)kb[j * d + c];",
                               "dot += (double)kb[j * d + c] * (double)kb[j * d + c];"),
     "key_operand_for_value": ("o[c] += p[j] * (double)vb[j * d + c];",
@@ -36,8 +41,8 @@ MUTANTS = {
     "empty_row_lse_zero": ("LSE[t] = -INFINITY;", "LSE[t] = 0.0;"),
     "value_row_skipped": ("for (int64_t j = 0; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +=",
                           "for (int64_t j = 1; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +="),
-    "query_row_off_by_one": ("const float *q  = Q + ((b * H + h) * N + i) * d;",
-                             "const float *q  = Q + ((b * H + h) * N + (i > 0 ? i - 1 : 0)) * d;"),
+    "query_row_off_by_one": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
+                             "const float *q  = Q + ((b * H + h) * Nq + (i > 0 ? i - 1 : 0)) * d;"),
 }
 
 
