@@ -35,6 +35,20 @@ One more workload measures the split-key forward:
 
 * ``prefill_shard8``: B=1 H=4 N=4096 d=128 fp16, causal: the prefill's
   per-GPU share when its 32 heads are divided among 8 GPUs.
+
+Three measure grouped-query and cross-attention (Q ``[B, H, Nq, d]``, K and
+V ``[B, Hkv, N, d]``, N the key length), which "cuda-reranker" lists as
+extensions; the pages give no shapes for them, so these reuse theirs:
+
+* ``gqa_prefill``: the prefill with 8 key/value heads for its 32 query heads
+  (4 query heads per key/value head), B=1 Nq=N=4096 d=128 fp16, causal.
+* ``gqa_decode``: one new query per sequence against a long key/value
+  history: B=8 H=32 Hkv=8 Nq=1 N=32768 (the long-context length) d=128
+  bf16, causal, valid history length uniform in [16384, 32768] per sequence.
+* ``cross``: cross-attention of 2048 queries over 4096 keys, B=4 H=16 d=64
+  fp16, no mask.
+
+Draw order for these is Q, K, V with their own shapes, then key lengths.
 """
 from __future__ import annotations
 
@@ -64,6 +78,8 @@ class Workload:
     v_sigma: float = 1.0
     seed: int = 0
     sample_rows: Optional[int] = None  # query rows per head the oracle checks
+    Hkv: Optional[int] = None  # key/value heads (None: H)
+    Nq: Optional[int] = None   # query rows per head (None: N, the key length)
 
     @property
     def scale(self) -> np.float32:
@@ -71,8 +87,26 @@ class Workload:
         return np.float32(1.0 / np.sqrt(np.float64(self.d)))
 
     @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
+
+    @property
+    def q_len(self) -> int:
+        return self.N if self.Nq is None else self.Nq
+
+    @property
+    def general(self) -> bool:
+        """Grouped key/value heads or a query length other than the key length."""
+        return self.kv_heads != self.H or self.q_len != self.N
+
+    @property
     def shape(self):
-        return (self.B, self.H, self.N, self.d)
+        """Q and O shape; K and V are ``kv_shape``."""
+        return (self.B, self.H, self.q_len, self.d)
+
+    @property
+    def kv_shape(self):
+        return (self.B, self.kv_heads, self.N, self.d)
 
 
 WORKLOADS = {
@@ -88,10 +122,15 @@ WORKLOADS = {
     # too few 256-row query tiles (64) to occupy the GPU, the shape the
     # split-key forward is for.
     "prefill_shard8": Workload("prefill_shard8", 1, 4, 4096, 128, F16, True, False, seed=1006),
+    # grouped-query and cross-attention shapes
+    "gqa_prefill": Workload("gqa_prefill", 1, 32, 4096, 128, F16, True, False, seed=1007, Hkv=8),
+    "gqa_decode": Workload("gqa_decode", 8, 32, 32768, 128, BF16, True, True,
+                           key_len_lo=16384, key_len_hi=32768, seed=1008, Hkv=8, Nq=1),
+    "cross": Workload("cross", 4, 16, 4096, 64, F16, False, False, seed=1009, Nq=2048),
 }
 WORKLOAD_ORDER = ["single_head", "reranker", "prefill", "peaky", "long_context"]
 # workloads beyond the five the pages' configurations describe
-EXTRA_WORKLOADS = ["prefill_shard8"]
+EXTRA_WORKLOADS = ["prefill_shard8", "gqa_prefill", "gqa_decode", "cross"]
 
 
 # ---------------------------------------------------------------- rounding
@@ -141,18 +180,19 @@ def _normal(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 def generate(w: Workload, seed: Optional[int] = None) -> dict:
     """Draw one workload's inputs.
 
-    Returns a dict with uint16 bit arrays ``Q, K, V`` of shape ``[B,H,N,d]``,
-    ``key_len`` (int32 ``[B]`` or None), ``rows`` (int64 ``[H, R]`` sampled
-    query rows per head, or None), and the scalars ``dtype``, ``scale``,
-    ``causal`` and ``seed``.
+    Returns a dict with uint16 bit arrays ``Q`` (``w.shape``), ``K`` and
+    ``V`` (``w.kv_shape``), ``key_len`` (int32 ``[B]`` or None), ``rows``
+    (int64 ``[H, R]`` sampled query rows per head, or None), and the scalars
+    ``dtype``, ``scale``, ``causal`` and ``seed``.
     """
     seed = w.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {"workload": w.name, "dtype": w.dtype, "scale": w.scale,
            "causal": w.causal, "seed": seed,
-           "B": w.B, "H": w.H, "N": w.N, "d": w.d}
-    for name, sigma in (("Q", w.q_sigma), ("K", w.k_sigma), ("V", w.v_sigma)):
-        out[name] = round_bits(_normal(rng, w.shape, sigma), w.dtype)
+           "B": w.B, "H": w.H, "N": w.N, "d": w.d, "Hkv": w.kv_heads, "Nq": w.q_len}
+    for name, sigma, shape in (("Q", w.q_sigma, w.shape), ("K", w.k_sigma, w.kv_shape),
+                               ("V", w.v_sigma, w.kv_shape)):
+        out[name] = round_bits(_normal(rng, shape, sigma), w.dtype)
     out["key_len"] = None
     if w.key_padding:
         out["key_len"] = rng.integers(w.key_len_lo, w.key_len_hi + 1,
@@ -160,7 +200,7 @@ def generate(w: Workload, seed: Optional[int] = None) -> dict:
     out["rows"] = None
     if w.sample_rows is not None:
         out["rows"] = np.stack([
-            np.sort(rng.choice(w.N, size=w.sample_rows, replace=False))
+            np.sort(rng.choice(w.q_len, size=w.sample_rows, replace=False))
             for _ in range(w.H)]).astype(np.int64)
     return out
 
@@ -179,6 +219,23 @@ def random_case(B: int, H: int, N: int, d: int, dtype: str, *, seed: int,
         out[name] = round_bits(_normal(rng, (B, H, N, d), sigma), dtype)
     if isinstance(key_len, str) and key_len == "random":
         key_len = rng.integers(0, N + 1, size=B)
+    out["key_len"] = None if key_len is None else np.asarray(key_len, dtype=np.int32)
+    return out
+
+
+def random_case_general(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, *,
+                        seed: int, sigma: float = 1.0, key_len=None) -> dict:
+    """Q ``[B, H, Nq, d]`` and K, V ``[B, Hkv, Nk, d]`` drawn as in random_case
+    (Q, K, V, then ``key_len``: None, a list, or ``"random"`` uniform in
+    [0, Nk])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"dtype": dtype, "seed": seed, "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "N": Nk,
+           "d": d, "scale": np.float32(1.0 / np.sqrt(np.float64(d)))}
+    out["Q"] = round_bits(_normal(rng, (B, H, Nq, d), sigma), dtype)
+    for name in ("K", "V"):
+        out[name] = round_bits(_normal(rng, (B, Hkv, Nk, d), sigma), dtype)
+    if isinstance(key_len, str) and key_len == "random":
+        key_len = rng.integers(0, Nk + 1, size=B)
     out["key_len"] = None if key_len is None else np.asarray(key_len, dtype=np.int32)
     return out
 

@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the fused exact-attention forward on one MI355X.
 
-A step is one attn_fwd launch over one batch of seeded synthetic inputs that
+A step is one forward call (attn_fwd, or attn_fwd_gqa for grouped-query and
+cross-attention shapes; their split-key forms when the shape has too few
+work items to fill the GPU) over one batch of seeded synthetic inputs that
 are already resident in device memory.  The K timed steps are recorded into
-one HIP graph and replayed, so no host time separates the launches.  The default workload is the causal
-decoder prefill B=1 H=32 N=4096 d=128 fp16 (scale 1/sqrt(128)), the
-configuration whose throughput is reported as TFLOP/s and as a fraction of
-the dense fp16 matrix-core peak.  Prints one JSON line.
+one HIP graph and replayed, so no host time separates the launches.  The
+default workload is the causal decoder prefill B=1 H=32 N=4096 d=128 fp16
+(scale 1/sqrt(128)), the configuration whose throughput is reported as
+TFLOP/s and as a fraction of the dense fp16 matrix-core peak.  Prints one
+JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--no-naive] [--no-graph]
+                  [--no-naive] [--no-graph] [--splitkv auto|on|off] [--kv-splits S]
   python bench.py --copy-probe       # a plain device copy of known size, for
                                      # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
@@ -48,10 +51,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle sample")
-    ap.add_argument("--splitkv", action="store_true",
-                    help="time attn_fwd_splitkv (default split count) instead of attn_fwd")
+    ap.add_argument("--splitkv", choices=["auto", "on", "off"], default="auto",
+                    help="time the split-key entry point: auto = when the library's "
+                         "default split count for the shape is above 1")
     ap.add_argument("--kv-splits", type=int, default=0,
-                    help="with --splitkv: this split count instead of the default")
+                    help="split count for the split-key entry point instead of the default")
     ap.add_argument("--no-graph", action="store_true",
                     help="time K plain launches instead of one replay of a graph of K launches")
     ap.add_argument("--no-naive", action="store_true",
@@ -60,35 +64,46 @@ def parse():
     return ap.parse_args()
 
 
-def metric_flops(w) -> float:
-    """The metric's FLOP count: 4 B H N^2 d, halved when causal."""
-    f = 4.0 * w.B * w.H * w.N * w.N * w.d
-    return f / 2 if w.causal else f
+def key_lengths(w, key_len=None) -> np.ndarray:
+    """Valid keys per sequence, clamped to [0, N]."""
+    if key_len is None:
+        return np.full(w.B, w.N, dtype=np.int64)
+    return np.clip(np.asarray(key_len, np.int64), 0, w.N)
+
+
+def visible_per_query(w, L: int) -> np.ndarray:
+    """Visible keys of each query row of a sequence with L valid keys: under
+    causal masking query i sees keys j <= i + N - Nq (aligned at the end)."""
+    i = np.arange(w.q_len, dtype=np.int64)
+    if not w.causal:
+        return np.full(w.q_len, L, dtype=np.int64)
+    return np.clip(np.minimum(L, i + w.N - w.q_len + 1), 0, None)
 
 
 def visible_pairs(w, key_len=None) -> int:
     """Visible (query, key) pairs: the algorithmic unit of work (4d flops each)."""
-    total = 0
-    for b in range(w.B):
-        L = w.N if key_len is None else int(min(max(key_len[b], 0), w.N))
-        if w.causal:
-            # sum over i of min(L, i + 1)
-            pairs = L * (L + 1) // 2 + (w.N - L) * L
-        else:
-            pairs = w.N * L
-        total += pairs * w.H
-    return total
+    return int(sum(int(visible_per_query(w, int(L)).sum()) * w.H for L in key_lengths(w, key_len)))
+
+
+def metric_flops(w) -> float:
+    """The metric's FLOP count: 4 B H N^2 d, halved when causal, for
+    self-attention; 4 d per visible (query, key) pair for the other shapes."""
+    if w.general:
+        return 4.0 * w.d * visible_pairs(w, None)
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
 
 
 def algorithmic_bytes(w, key_len=None) -> int:
-    """Q and O once, K and V rows once per visible row, LSE once (4 B per row)."""
+    """Q and O once, each key/value head's visible K and V rows once, LSE once
+    (4 B per query row)."""
     elem = 2
-    qo = 2 * w.B * w.H * w.N * w.d * elem
+    qo = 2 * w.B * w.H * w.q_len * w.d * elem
     kv = 0
-    for b in range(w.B):
-        L = w.N if key_len is None else int(min(max(key_len[b], 0), w.N))
-        kv += 2 * w.H * L * w.d * elem
-    return qo + kv + w.B * w.H * w.N * 4
+    for L in key_lengths(w, key_len):
+        seen = int(visible_per_query(w, int(L)).max()) if w.q_len > 0 else 0
+        kv += 2 * w.kv_heads * seen * w.d * elem
+    return qo + kv + w.B * w.H * w.q_len * 4
 
 
 def source_digest() -> str:
@@ -171,34 +186,31 @@ def cpu_baseline(w, case, target_s: float):
     K = ai.bits_to_f32(case["K"], dt)
     V = ai.bits_to_f32(case["V"], dt)
     kl = case["key_len"]
+    Ls = key_lengths(w, kl)
+    vis = {int(L): visible_per_query(w, int(L)) for L in set(Ls.tolist())}
     rng = np.random.Generator(np.random.PCG64(w.seed + 31))
 
     def rows_flops(sel):
-        f = 0
-        for b, h, i in sel:
-            L = w.N if kl is None else int(min(max(kl[b], 0), w.N))
-            n = min(L, i + 1) if w.causal else L
-            f += 4 * w.d * n
-        return f
+        return sum(4 * w.d * int(vis[int(Ls[b])][i]) for b, h, i in sel)
 
     def pick(per_head):
         out = []
         for b in range(w.B):
             for h in range(w.H):
-                for i in rng.choice(w.N, size=per_head, replace=False):
+                for i in rng.choice(w.q_len, size=per_head, replace=False):
                     out.append((b, h, int(i)))
         return np.asarray(out, np.int64)
 
-    sel = pick(2)
+    sel = pick(min(2, w.q_len))
     t0 = time.perf_counter()
-    oracle.sdpa_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
     rate = rows_flops(sel) / max(time.perf_counter() - t0, 1e-6)
-    per_row = 4 * w.d * (w.N / 2 if w.causal else w.N)
-    per_head = int(max(1, min(w.N, target_s * rate / per_row / (w.B * w.H))))
+    per_row = max(1.0, 4 * w.d * float(np.mean([v.mean() for v in vis.values()])))
+    per_head = int(max(1, min(w.q_len, target_s * rate / per_row / (w.B * w.H))))
     sel = pick(per_head)
     flops = rows_flops(sel)
     t0 = time.perf_counter()
-    oracle.sdpa_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
     secs = time.perf_counter() - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
@@ -235,18 +247,31 @@ def main():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     scale = float(w.scale)
     code = attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16
+    default_splits = attn.attn_fwd_gqa_splitkv_default_splits(
+        code, w.B, w.H, w.kv_heads, w.q_len, w.N, w.d, w.causal)
+    use_split = args.splitkv == "on" or (args.splitkv == "auto" and
+                                         (args.kv_splits > 1 or default_splits > 1))
     n_splits = None
-    if args.splitkv:
-        n_splits = args.kv_splits if args.kv_splits > 0 else \
-            attn.attn_fwd_splitkv_default_splits(code, w.B, w.H, w.N, w.d, w.causal)
-        ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, n_splits) // 4,
+    if use_split:
+        n_splits = args.kv_splits if args.kv_splits > 0 else default_splits
+        ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.q_len, w.d,
+                                                               n_splits) // 4,
                          dtype=torch.float32, device=dev)
+    if w.general:
+        entry = "attn_fwd_gqa_splitkv" if use_split else "attn_fwd_gqa"
+    else:
+        entry = "attn_fwd_splitkv" if use_split else "attn_fwd"
 
     def step():
         # on the current stream (the capture stream while a graph records)
-        if n_splits is not None:
+        if entry == "attn_fwd_splitkv":
             attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits, scale=scale,
                                   causal=w.causal, key_len=kl)
+        elif entry == "attn_fwd_gqa_splitkv":
+            attn.attn_fwd_gqa_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
+                                      scale=scale, causal=w.causal, key_len=kl)
+        elif entry == "attn_fwd_gqa":
+            attn.attn_fwd_gqa(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
         else:
             attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
 
@@ -296,10 +321,12 @@ def main():
     pairs = visible_pairs(w, key_len)
     F_alg = 4.0 * w.d * pairs
     kernel = attn.attn_fwd_kernel_name(code, w.d, w.N, w.causal, key_len is not None)
-    if n_splits is not None:
-        kernel = kernel.replace("attn_fwd_", "attn_fwd_split_", 1)
-    if w.key_padding:
-        nbytes = algorithmic_bytes(w, key_len)
+    if n_splits is not None:  # the split form always runs the streaming kernel
+        kernel = f"attn_fwd_split_d{w.d}_{w.dtype}_{'causal' if w.causal else 'full'}"
+    nbytes = algorithmic_bytes(w, key_len)
+    # the bound: HBM when the flops per algorithmic byte are below the
+    # machine balance (matrix-core peak / HBM bandwidth), else the matrix cores
+    if F_alg / nbytes < MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
         achieved = nbytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
@@ -317,18 +344,20 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
         "launch": "plain" if args.no_graph else "hip_graph",
-        "entry": "attn_fwd_splitkv" if n_splits is not None else "attn_fwd",
+        "entry": entry,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "Hkv": w.kv_heads, "Nq": w.q_len,
                    "causal": w.causal, "key_padding": w.key_padding, "seed": w.seed,
                    "kv_splits": n_splits,
                    "global_batch": w.B, "seq_len": w.N},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
         "roofline": roof,
     }
-    if not args.no_naive:
+    # the unfused baseline takes self-attention shapes only
+    if not args.no_naive and not w.general:
         nb = naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F)
         nb["fused_speedup"] = nb["ms_per_step"] / ms_per_step
         out["naive_baseline"] = nb

@@ -7,7 +7,7 @@ status into ``AttnError``.  All arithmetic runs in the HIP kernels.  PyTorch
 supplies device memory and streams.
 
 Importing this package raises ImportError when libattn.so has not been built
-(``python -m exact_self_attention_amd.build``); there is no fallback.
+(``python exact_self_attention_amd/build.py``); there is no fallback.
 """
 from __future__ import annotations
 
@@ -25,9 +25,9 @@ ATTN_BF16 = 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_MISALIGNED", 4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH",
           6: "ATTN_ERR_DEVICE"}
-EXPORTS = ["attn_fwd", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
-           "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-           "attn_fwd_splitkv_default_splits",
+EXPORTS = ["attn_fwd", "attn_fwd_gqa", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
+           "attn_fwd_splitkv", "attn_fwd_gqa_splitkv", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_splitkv_default_splits", "attn_fwd_gqa_splitkv_default_splits",
            "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
 
 
@@ -40,12 +40,19 @@ class AttnError(RuntimeError):
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "'python -m exact_self_attention_amd.build' (hipcc, gfx950)")
+                          "'python exact_self_attention_amd/build.py' (hipcc, gfx950)")
     lib = ctypes.CDLL(path)
     p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     common = [i32, p, p, p, p, p, i64, i64, i64, i64, f32, i32, p]
     lib.attn_fwd.argtypes = common + [p]
     lib.attn_fwd.restype = i32
+    general = [i32, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32, p]
+    lib.attn_fwd_gqa.argtypes = general + [p]
+    lib.attn_fwd_gqa.restype = i32
+    lib.attn_fwd_gqa_splitkv.argtypes = general + [i64, p, ctypes.c_size_t, p]
+    lib.attn_fwd_gqa_splitkv.restype = i32
+    lib.attn_fwd_gqa_splitkv_default_splits.argtypes = [i32, i64, i64, i64, i64, i64, i64, i32]
+    lib.attn_fwd_gqa_splitkv_default_splits.restype = i64
     lib.attn_fwd_naive.argtypes = common + [p, ctypes.c_size_t, p]
     lib.attn_fwd_naive.restype = i32
     lib.attn_fwd_naive_workspace_bytes.argtypes = [i64, i64, i64]
@@ -102,6 +109,64 @@ def _check_tensors(q, k, v, o, lse, key_len):
         if key_len.dtype != torch.int32 or tuple(key_len.shape) != (q.shape[0],) \
                 or not key_len.is_contiguous() or key_len.device != q.device:
             raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
+
+
+def _check_general(q, k, v, o, lse, key_len):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape [B, H, Nq, d]")
+    if v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    if not q.is_cuda:
+        raise ValueError("tensors must live on a GPU")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) \
+                or not lse.is_contiguous() or lse.device != q.device:
+            raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or tuple(key_len.shape) != (q.shape[0],) \
+                or not key_len.is_contiguous() or key_len.device != q.device:
+            raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
+
+
+def attn_fwd_gqa(q, k, v, o, lse=None, *, scale: float, causal: bool = False,
+                 key_len=None, stream=None) -> None:
+    """Fused forward, general shapes: q, o [B, H, Nq, d]; k, v [B, Hkv, Nk, d]."""
+    code = _dtype_code(q)
+    _check_general(q, k, v, o, lse, key_len)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    st = lib.attn_fwd_gqa(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                          B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(key_len),
+                          _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_gqa", st)
+
+
+def attn_fwd_gqa_splitkv(q, k, v, o, lse=None, *, workspace: torch.Tensor, n_splits: int,
+                         scale: float, causal: bool = False, key_len=None, stream=None) -> None:
+    """attn_fwd_gqa over ``n_splits`` key ranges, merged (see include/attn.h)."""
+    code = _dtype_code(q)
+    _check_general(q, k, v, o, lse, key_len)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_gqa_splitkv(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                  _ptr(key_len), int(n_splits), _ptr(workspace), nbytes,
+                                  _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_gqa_splitkv", st)
+
+
+def attn_fwd_gqa_splitkv_default_splits(dtype: int, B: int, H: int, Hkv: int, Nq: int, Nk: int,
+                                        d: int, causal: bool) -> int:
+    return int(lib.attn_fwd_gqa_splitkv_default_splits(dtype, B, H, Hkv, Nq, Nk, d,
+                                                       int(bool(causal))))
 
 
 def attn_fwd(q, k, v, o, lse=None, *, scale: float, causal: bool = False,

@@ -29,41 +29,82 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Checks shared by attn_fwd and attn_fwd_naive.  *empty is set when there is
-// nothing to compute (B*H*N == 0).
+// Problem shape: Q and O are [B, H, Nq, d], K and V [B, Hkv, Nk, d].
+struct Shape {
+    int64_t B, H, Hkv, Nq, Nk, d;
+    size_t q_elems() const { return (size_t)B * (size_t)H * (size_t)Nq; }   // rows of Q, O, LSE
+    size_t kv_elems() const { return (size_t)B * (size_t)Hkv * (size_t)Nk; }  // rows of K, V
+};
+
+// Checks shared by every forward entry point.  *empty is set when there is
+// nothing to compute (B*H*Nq == 0).  Nk == 0 is not empty: every row then
+// has no visible key (O = 0, LSE = -inf), and K and V may be null.
 attn_status_t check_args(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
-                         const void *O, const float *LSE, int64_t B, int64_t H, int64_t N,
-                         int64_t d, float scale, const int32_t *key_len, bool *empty) {
+                         const void *O, const float *LSE, const Shape &sh, float scale,
+                         const int32_t *key_len, bool *empty) {
     *empty = false;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_INVALID_ARG;
-    if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-    if (N > kMaxN) return ATTN_ERR_INVALID_ARG;
-    if (B > 0 && H > INT32_MAX / B) return ATTN_ERR_INVALID_ARG;
+    if (sh.B < 0 || sh.H < 0 || sh.Hkv < 0 || sh.Nq < 0 || sh.Nk < 0) return ATTN_ERR_INVALID_ARG;
+    if (sh.d != 32 && sh.d != 64 && sh.d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (sh.Nq > kMaxN || sh.Nk > kMaxN) return ATTN_ERR_INVALID_ARG;
+    if (sh.H > 0 && (sh.Hkv == 0 || sh.Hkv > sh.H || sh.H % sh.Hkv != 0)) return ATTN_ERR_INVALID_ARG;
+    if (sh.B > 0 && sh.H > INT32_MAX / sh.B) return ATTN_ERR_INVALID_ARG;
+    // query rows per slice (the heads that share a key/value head)
+    if (sh.H > 0 && (sh.H / sh.Hkv) * sh.Nq > kMaxN) return ATTN_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
-    if (B == 0 || H == 0 || N == 0) {
+    if (sh.B == 0 || sh.H == 0 || sh.Nq == 0) {
         *empty = true;
         return ATTN_OK;
     }
-    if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (Q == nullptr || O == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (sh.Nk > 0 && (K == nullptr || V == nullptr)) return ATTN_ERR_INVALID_ARG;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
         return ATTN_ERR_MISALIGNED;
     if (!aligned(LSE, 4) || !aligned(key_len, 4)) return ATTN_ERR_MISALIGNED;
-    const size_t elems = (size_t)B * (size_t)H * (size_t)N;
-    const size_t tbytes = elems * (size_t)d * 2;
-    const size_t lbytes = elems * sizeof(float);
-    const size_t kbytes = (size_t)B * sizeof(int32_t);
-    if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) ||
-        overlaps(O, tbytes, V, tbytes))
+    const size_t qbytes = sh.q_elems() * (size_t)sh.d * 2;
+    const size_t kvbytes = sh.kv_elems() * (size_t)sh.d * 2;
+    const size_t lbytes = sh.q_elems() * sizeof(float);
+    const size_t kbytes = (size_t)sh.B * sizeof(int32_t);
+    if (overlaps(O, qbytes, Q, qbytes) || overlaps(O, qbytes, K, kvbytes) ||
+        overlaps(O, qbytes, V, kvbytes))
         return ATTN_ERR_INVALID_ARG;
     if (LSE != nullptr &&
-        (overlaps(LSE, lbytes, Q, tbytes) || overlaps(LSE, lbytes, K, tbytes) ||
-         overlaps(LSE, lbytes, V, tbytes) || overlaps(LSE, lbytes, O, tbytes)))
+        (overlaps(LSE, lbytes, Q, qbytes) || overlaps(LSE, lbytes, K, kvbytes) ||
+         overlaps(LSE, lbytes, V, kvbytes) || overlaps(LSE, lbytes, O, qbytes)))
         return ATTN_ERR_INVALID_ARG;
     if (key_len != nullptr &&
-        (overlaps(key_len, kbytes, O, tbytes) || overlaps(key_len, kbytes, LSE, lbytes)))
+        (overlaps(key_len, kbytes, O, qbytes) || overlaps(key_len, kbytes, LSE, lbytes)))
         return ATTN_ERR_INVALID_ARG;
     return ATTN_OK;
+}
+
+// Kernel arguments for a checked, non-empty problem.
+attn::FwdParams make_params(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                            const Shape &sh, float scale, const int32_t *key_len) {
+    attn::FwdParams p;
+    p.Q = static_cast<const uint16_t *>(Q);
+    p.K = static_cast<const uint16_t *>(K);
+    p.V = static_cast<const uint16_t *>(V);
+    p.O = static_cast<uint16_t *>(O);
+    p.LSE = LSE;
+    p.key_len = key_len;
+    p.M = (sh.H / sh.Hkv) * sh.Nq;
+    p.Nk = sh.Nk;
+    p.Nq = (int)sh.Nq;
+    p.causal_off = (int)(sh.Nk - sh.Nq);
+    p.slices = (int)(sh.B * sh.Hkv);
+    p.Hkv = (int)sh.Hkv;
+    p.n_qtiles = 0;
+    p.kv_splits = 1;
+    p.split_tiles = 0;
+    p.part_O = nullptr;
+    p.part_LSE = nullptr;
+    // The kernel needs a positive exp2 scale (masked scores are -inf and must
+    // map to exactly 0).  A zero scale becomes 1e-30: every score times it
+    // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
+    return p;
 }
 
 // The current device must be a gfx950; checked once per device.
@@ -86,37 +127,26 @@ attn_status_t check_device() {
 
 extern "C" {
 
-attn_status_t attn_fwd(attn_dtype_t dtype, const void *Q, const void *K, const void *V, void *O,
-                       float *LSE, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                       int causal, const int32_t *key_len, void *stream) {
+attn_status_t attn_fwd_gqa(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                           void *O, float *LSE, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                           int64_t Nk, int64_t d, float scale, int causal,
+                           const int32_t *key_len, void *stream) {
+    const Shape sh{B, H, Hkv, Nq, Nk, d};
     bool empty = false;
-    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, sh, scale, key_len, &empty);
     if (st != ATTN_OK || empty) return st;
     st = check_device();
     if (st != ATTN_OK) return st;
-    attn::FwdParams p;
-    p.Q = static_cast<const uint16_t *>(Q);
-    p.K = static_cast<const uint16_t *>(K);
-    p.V = static_cast<const uint16_t *>(V);
-    p.O = static_cast<uint16_t *>(O);
-    p.LSE = LSE;
-    p.key_len = key_len;
-    p.N = N;
-    p.BH = (int)(B * H);
-    p.H = (int)H;
-    p.n_qtiles = 0;
-    p.kv_splits = 1;
-    p.split_tiles = 0;
-    p.part_O = nullptr;
-    p.part_LSE = nullptr;
-    // The kernel needs a positive exp2 scale (masked scores are -inf and must
-    // map to exactly 0).  A zero scale becomes 1e-30: every score times it
-    // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
+    const attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
     const hipError_t e = attn::launch_fwd(dtype == ATTN_BF16, (int)d, causal != 0, p,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd(attn_dtype_t dtype, const void *Q, const void *K, const void *V, void *O,
+                       float *LSE, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       int causal, const int32_t *key_len, void *stream) {
+    return attn_fwd_gqa(dtype, Q, K, V, O, LSE, B, H, H, N, N, d, scale, causal, key_len, stream);
 }
 
 attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
@@ -124,7 +154,8 @@ attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, c
                              float scale, int causal, const int32_t *key_len, void *workspace,
                              size_t workspace_bytes, void *stream) {
     bool empty = false;
-    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    attn_status_t st =
+        check_args(dtype, Q, K, V, O, LSE, Shape{B, H, H, N, N, d}, scale, key_len, &empty);
     if (st != ATTN_OK || empty) return st;
     if ((N + 15) / 16 > 65535) return ATTN_ERR_INVALID_ARG;  // grid limit of the score kernel
     const size_t per_head = attn_fwd_naive_workspace_bytes(1, 1, N);
@@ -168,25 +199,28 @@ attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, c
     return ATTN_OK;
 }
 
-attn_status_t attn_fwd_splitkv(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
-                               void *O, float *LSE, int64_t B, int64_t H, int64_t N, int64_t d,
-                               float scale, int causal, const int32_t *key_len, int64_t n_splits,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
+                                   const void *V, void *O, float *LSE, int64_t B, int64_t H,
+                                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                   int causal, const int32_t *key_len, int64_t n_splits,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    const Shape sh{B, H, Hkv, Nq, Nk, d};
     bool empty = false;
-    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, B, H, N, d, scale, key_len, &empty);
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, sh, scale, key_len, &empty);
     if (st != ATTN_OK) return st;
     if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
     if (empty) return ATTN_OK;
-    const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits);
+    const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits);
     if (need == 0) return ATTN_ERR_INVALID_ARG;
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_MISALIGNED;
-    const size_t elems = (size_t)B * (size_t)H * (size_t)N;
-    if (overlaps(workspace, workspace_bytes, Q, elems * d * 2) ||
-        overlaps(workspace, workspace_bytes, K, elems * d * 2) ||
-        overlaps(workspace, workspace_bytes, V, elems * d * 2) ||
-        overlaps(workspace, workspace_bytes, O, elems * d * 2) ||
-        overlaps(workspace, workspace_bytes, LSE, LSE ? elems * 4 : 0) ||
+    const size_t qbytes = sh.q_elems() * (size_t)d * 2;
+    const size_t kvbytes = sh.kv_elems() * (size_t)d * 2;
+    if (overlaps(workspace, workspace_bytes, Q, qbytes) ||
+        overlaps(workspace, workspace_bytes, K, kvbytes) ||
+        overlaps(workspace, workspace_bytes, V, kvbytes) ||
+        overlaps(workspace, workspace_bytes, O, qbytes) ||
+        overlaps(workspace, workspace_bytes, LSE, LSE ? sh.q_elems() * 4 : 0) ||
         overlaps(workspace, workspace_bytes, key_len, key_len ? (size_t)B * 4 : 0))
         return ATTN_ERR_INVALID_ARG;
     st = check_device();
@@ -194,29 +228,25 @@ attn_status_t attn_fwd_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
 
     // whole 64-key tiles per split; trailing splits that would be empty for
     // every row are not launched
-    const int64_t tiles = (N + 63) / 64;
-    const int64_t per = (tiles + n_splits - 1) / n_splits;
-    const int64_t used = (tiles + per - 1) / per;
-    attn::FwdParams p;
-    p.Q = static_cast<const uint16_t *>(Q);
-    p.K = static_cast<const uint16_t *>(K);
-    p.V = static_cast<const uint16_t *>(V);
-    p.O = static_cast<uint16_t *>(O);
-    p.LSE = LSE;
-    p.key_len = key_len;
-    p.N = N;
-    p.BH = (int)(B * H);
-    p.H = (int)H;
-    p.n_qtiles = 0;
+    const int64_t tiles = (Nk + 63) / 64;
+    const int64_t per = tiles > 0 ? (tiles + n_splits - 1) / n_splits : 1;
+    const int64_t used = tiles > 0 ? (tiles + per - 1) / per : 1;
+    attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
     p.kv_splits = (int)used;
     p.split_tiles = (int)per;
     p.part_O = static_cast<float *>(workspace);
-    p.part_LSE = p.part_O + (size_t)used * elems * (size_t)d;
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
+    p.part_LSE = p.part_O + (size_t)used * sh.q_elems() * (size_t)d;
     const hipError_t e = attn::launch_fwd_split(dtype == ATTN_BF16, (int)d, causal != 0, p,
                                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd_splitkv(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                               void *O, float *LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                               float scale, int causal, const int32_t *key_len, int64_t n_splits,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    return attn_fwd_gqa_splitkv(dtype, Q, K, V, O, LSE, B, H, H, N, N, d, scale, causal, key_len,
+                                n_splits, workspace, workspace_bytes, stream);
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
@@ -231,23 +261,31 @@ size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t
     return (size_t)total;
 }
 
-int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
-                                        int64_t d, int causal) {
+int64_t attn_fwd_gqa_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H,
+                                            int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                            int causal) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return 1;
     if (d != 32 && d != 64 && d != 128) return 1;
-    if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN || H > INT32_MAX / B) return 1;
+    if (B <= 0 || H <= 0 || Hkv <= 0 || Hkv > H || H % Hkv != 0 || Nq <= 0 || Nk <= 0 ||
+        Nq > kMaxN || Nk > kMaxN || H > INT32_MAX / B || (H / Hkv) * Nq > kMaxN)
+        return 1;
     if (check_device() != ATTN_OK) return 1;
     const int resident = attn::fwd_split_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0);
     if (resident <= 0) return 1;
     const int64_t rows = attn::fwd_query_rows_per_item();
-    const int64_t items = (N + rows - 1) / rows * B * H;
+    const int64_t items = ((H / Hkv) * Nq + rows - 1) / rows * B * Hkv;
     if (items >= resident) return 1;
-    const int64_t tiles = (N + 63) / 64;
+    const int64_t tiles = (Nk + 63) / 64;
     int64_t s = (resident + items - 1) / items;
     const int64_t max_s = tiles / 2 > 1 ? tiles / 2 : 1;
     if (s > max_s) s = max_s;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
+}
+
+int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
+                                        int64_t d, int causal) {
+    return attn_fwd_gqa_splitkv_default_splits(dtype, B, H, H, N, N, d, causal);
 }
 
 size_t attn_fwd_naive_workspace_bytes(int64_t B, int64_t H, int64_t N) {
@@ -264,7 +302,7 @@ const char *attn_status_string(attn_status_t status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument (size, scale, null pointer or aliasing)";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype (d must be 32, 64 or 128)";
     case ATTN_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, LSE and key_len 4)";
-    case ATTN_ERR_WORKSPACE: return "naive workspace missing or smaller than one head's N*N*4 bytes";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than the entry point needs";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
     }

@@ -200,5 +200,43 @@ __device__ __forceinline__ float exps64(const f32x16 (&s)[2], float c, float neg
     return pr[0];
 }
 
+// Causal positions of a slice's query rows.  The rows of the query heads
+// that share a key/value head follow each other, nq rows per head, so row r
+// is query r mod nq of its head and sees keys j <= r mod nq + off.
+struct CausalRows {
+    int nq;   // query rows per head
+    int off;  // keys minus query rows per head
+    __device__ __forceinline__ int pos(int r) const { return r % nq + off; }
+    // Lowest and highest position among rows r_lo .. r_hi (r_lo <= r_hi).
+    // Rows on both sides of a head boundary include a first row (position
+    // off) and a last one (position nq - 1 + off).
+    __device__ __forceinline__ void range(int r_lo, int r_hi, int &lo, int &hi) const {
+        const int h_lo = r_lo / nq, h_hi = r_hi / nq;
+        if (h_lo == h_hi) {
+            lo = r_lo - h_lo * nq + off;
+            hi = r_hi - h_hi * nq + off;
+        } else {
+            lo = off;
+            hi = nq - 1 + off;
+        }
+    }
+};
+
+// Launch order of a slice's query tiles (rows_per_tile rows each) under a
+// causal mask, most visible keys first, so that the last workgroups to start
+// are the cheapest.  A tile's work grows with its rows' positions.  When each
+// head's nq rows split into whole tiles, tile t of every one of the m / nq
+// heads has the same work: launch index i then goes over t downwards and,
+// for each t, over the heads.  Otherwise the tiles go from last to first.
+__device__ __forceinline__ int heavy_first_tile(int i, int n_tiles, int nq, int m,
+                                                int rows_per_tile) {
+    const int heads = m / nq;
+    if (heads > 1 && nq % rows_per_tile == 0) {
+        const int per_head = nq / rows_per_tile;
+        return (i % heads) * per_head + (per_head - 1 - i / heads);
+    }
+    return n_tiles - 1 - i;
+}
+
 }  // namespace cdna4
 }  // namespace attn

@@ -1,7 +1,9 @@
 // Fused exact attention forward for gfx950 (CDNA4).
 //
-// One workgroup = 8 waves = one tile of 256 query rows of one (b, h); each
-// wave owns 32 query rows.  Key/value tiles of 64 rows stream through LDS.
+// One workgroup = 8 waves = one tile of 256 query rows of one slice (b,
+// key/value head: the rows of the query heads that share it, head after
+// head); each wave owns 32 query rows.  Key/value tiles of 64 rows stream
+// through LDS.
 // Per key tile j, each wave computes
 //
 //   S^T = K_j Q^T            32x32x16 MFMA, fp16/bf16 in, fp32 out
@@ -135,39 +137,52 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int simd = wave & 3;
     const int rb = 2 * simd + grp;   // this wave's 32-row block in the tile
 
-    const int BH = p.BH;
-    // workgroup -> (key split, query tile, head)
-    const int per_split = p.n_qtiles * BH;
+    const int S = p.slices;
+    // workgroup -> (key split, query tile, slice)
+    const int per_split = p.n_qtiles * S;
     const int sp = SPLIT ? (int)blockIdx.x / per_split : 0;
     const int wg = (int)blockIdx.x - sp * per_split;
-    const int bh = wg % BH;
-    int qt = wg / BH;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
-    const int N = (int)p.N;
-    const int b = bh / p.H;
-    const size_t base = (size_t)bh * (size_t)N * D;
-    const uint16_t *__restrict__ Qp = p.Q + base;
-    const uint16_t *__restrict__ Kp = p.K + base;
-    const uint16_t *__restrict__ Vp = p.V + base;
+    const int sl = wg % S;
+    int qt = wg / S;
+    const int M = (int)p.M;                // query rows of the slice
+    if (CAUSAL) qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kBM);
+    const int Nk = (int)p.Nk;
+    const int b = sl / p.Hkv;
+    const size_t q_base = (size_t)sl * (size_t)M * D;
+    const size_t kv_base = (size_t)sl * (size_t)Nk * D;
+    const uint16_t *__restrict__ Qp = p.Q + q_base;
+    const uint16_t *__restrict__ Kp = p.K + kv_base;
+    const uint16_t *__restrict__ Vp = p.V + kv_base;
 
-    int Lk = N;
+    int Lk = Nk;
     if (p.key_len != nullptr) {
         const int v = p.key_len[b];
-        Lk = v < 0 ? 0 : (v > N ? N : v);
+        Lk = v < 0 ? 0 : (v > Nk ? Nk : v);
     }
     const int q0 = qt * kBM;
+    const int qw0 = q0 + rb * kQRows;
+    const int my_q = qw0 + l32;
+    const bool q_ok = my_q < M;
+    // causal: the workgroup needs keys up to the highest position of its
+    // rows, a wave up to the highest of its own; tiles past the lowest
+    // position of a wave's rows need per-element masking
+    const CausalRows cr{p.Nq, p.causal_off};
     int kv_end = Lk;
-    if (CAUSAL) kv_end = min(kv_end, q0 + kBM);
+    int wave_lo = 0, wave_hi = 0;
+    if (CAUSAL) {
+        int lo, hi;
+        cr.range(q0, min(q0 + kBM, M) - 1, lo, hi);
+        kv_end = max(0, min(kv_end, hi + 1));
+        if (qw0 < M) cr.range(qw0, min(qw0 + kQRows, M) - 1, wave_lo, wave_hi);
+    }
+    const int my_pos = CAUSAL ? cr.pos(my_q) : 0;
     // key tiles j_begin .. j_begin + n - 1 (all visible tiles unless split)
     const int n_all = (kv_end + kBN - 1) / kBN;
     const int j_begin = SPLIT ? sp * p.split_tiles : 0;
     const int n = SPLIT ? max(0, min(n_all - j_begin, p.split_tiles)) : n_all;
-    const int qw0 = q0 + rb * kQRows;
-    const int my_q = qw0 + l32;
-    const bool q_ok = my_q < N;
     int n_w = n;                                  // key tiles this wave computes
-    if (CAUSAL) n_w = max(0, min(n, (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN - j_begin));
-    if (qw0 >= N) n_w = 0;
+    if (CAUSAL) n_w = max(0, min(n, (max(0, min(kv_end, wave_hi + 1)) + kBN - 1) / kBN - j_begin));
+    if (qw0 >= M) n_w = 0;
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // The query tile goes to LDS once (same swizzled row-major layout as the
@@ -176,7 +191,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     {
         constexpr int QI = kBM * CPR / 64;        // 1 KB load instructions
         static_assert(QI % kWaves == 0, "query tile load split");
-        const int rows = min(kBM, N - q0);
+        const int rows = min(kBM, M - q0);
         const i32x4 rq = make_rsrc(Qp + (size_t)q0 * D, (uint32_t)(rows * D * 2));
         const uint32_t lds = (uint32_t)(uintptr_t)(lds_void *)sQ;
 #pragma unroll
@@ -337,14 +352,14 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     auto exps = [&](float neg_m) -> float { return exps64<BF16>(s, c, neg_m, pf); };
     auto softmax = [&](int j) {
         const int j0 = (j + j_begin) * kBN;
-        const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0);
+        const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > wave_lo);
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool ok = key < Lk && (!CAUSAL || key <= my_q);
+                    const bool ok = key < Lk && (!CAUSAL || key <= my_pos);
                     s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
         }
@@ -458,7 +473,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         // with no visible key in the split gets only LSE = -inf (the merge
         // then ignores its output)
         if (q_ok) {
-            const size_t row = ((size_t)sp * BH + bh) * (size_t)N + my_q;
+            const size_t row = ((size_t)sp * S + sl) * (size_t)M + my_q;
             float *orow = p.part_O + row * D;
             if (l_tot > 0.f)
 #pragma unroll
@@ -473,7 +488,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                 p.part_LSE[row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
         }
     } else if (q_ok) {
-        uint16_t *orow = p.O + base + (size_t)my_q * D;
+        uint16_t *orow = p.O + q_base + (size_t)my_q * D;
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
@@ -483,7 +498,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                 *reinterpret_cast<u32x2 *>(orow + cb * 32 + a * 8 + g * 4) = w;
             }
         if (p.LSE != nullptr && g == 0)
-            p.LSE[(size_t)bh * N + my_q] =
+            p.LSE[(size_t)sl * M + my_q] =
                 l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
@@ -538,7 +553,7 @@ struct MergeParams {
     const float *part_LSE;
     uint16_t *O;
     float *LSE;
-    int64_t rows;  // B * H * N
+    int64_t rows;  // B * H * Nq
     int d;
     int splits;
 };
@@ -624,8 +639,8 @@ const char *fwd_fused_kernel_name(bool bf16, int d, bool causal) {
 }
 
 hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
-    p.n_qtiles = (int)((p.N + kBM - 1) / kBM);
-    const int64_t blocks = (int64_t)p.n_qtiles * p.BH;
+    p.n_qtiles = (int)((p.M + kBM - 1) / kBM);
+    const int64_t blocks = (int64_t)p.n_qtiles * p.slices;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(entry(bf16, d, causal).fn, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
@@ -659,8 +674,8 @@ int fwd_split_resident_workgroups(bool bf16, int d, bool causal) {
 }
 
 hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
-    p.n_qtiles = (int)((p.N + kBM - 1) / kBM);
-    const int64_t blocks = (int64_t)p.n_qtiles * p.BH * p.kv_splits;
+    p.n_qtiles = (int)((p.M + kBM - 1) / kBM);
+    const int64_t blocks = (int64_t)p.n_qtiles * p.slices * p.kv_splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL || p.kv_splits < 1 || p.split_tiles < 1)
         return hipErrorInvalidConfiguration;
@@ -673,7 +688,7 @@ hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStrea
     m.part_LSE = p.part_LSE;
     m.O = p.O;
     m.LSE = p.LSE;
-    m.rows = (int64_t)p.BH * p.N;
+    m.rows = (int64_t)p.slices * p.M;
     m.d = d;
     m.splits = p.kv_splits;
     const int64_t threads = m.rows * (d / 4);

@@ -1,11 +1,12 @@
 // Fused exact attention forward for short sequences on gfx950 (CDNA4).
 //
-// When a head's visible keys fit in LDS (N <= 256 at d <= 64, N <= 128 at
+// When a slice's keys fit in LDS (Nk <= 256 at d <= 64, Nk <= 128 at
 // d = 128) the streaming pipeline of the long-sequence kernel only adds
 // latency: every tile is used once and the loop is a few tiles long.  Here a
-// workgroup of 4 waves owns 128 query rows of one (b, h):
+// workgroup of 4 waves owns 128 query rows of one slice (b, key/value head;
+// the rows of the query heads that share it, head after head):
 //
-//   1. all of the head's visible K and V rows go to LDS at once (direct
+//   1. all of the slice's visible K and V rows go to LDS at once (direct
 //      buffer loads, rows past the valid key length read as zero and are not
 //      fetched), and each wave loads the Q fragments of its query rows
 //      straight into VGPRs;
@@ -36,7 +37,7 @@ using namespace cdna4;
 
 constexpr int short_max_keys_of(int d) { return d >= 128 ? 128 : 256; }
 // 4 waves, one per SIMD and per 32 query rows: a workgroup owns 128 query
-// rows of one (b, h).  (One 8-wave workgroup per head, or one 4-wave
+// rows of one slice.  (One 8-wave workgroup per head, or one 4-wave
 // workgroup making two passes, measured slower: fewer waves in flight.)
 constexpr int kSWaves = 4;
 constexpr int kSBM = kSWaves * kQRows;
@@ -68,34 +69,47 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     const int g = lane >> 5;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-    const int BH = p.BH;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
-    const int N = (int)p.N;
-    const int b = bh / p.H;
-    const size_t base = (size_t)bh * (size_t)N * D;
-    const uint16_t *__restrict__ Qp = p.Q + base;
-    const uint16_t *__restrict__ Kp = p.K + base;
-    const uint16_t *__restrict__ Vp = p.V + base;
+    const int S = p.slices;
+    const int sl = blockIdx.x % S;
+    int qt = blockIdx.x / S;
+    const int M = (int)p.M;                // query rows of the slice
+    if (CAUSAL) qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kSBM);
+    const int Nk = (int)p.Nk;
+    const int b = sl / p.Hkv;
+    const size_t q_base = (size_t)sl * (size_t)M * D;
+    const size_t kv_base = (size_t)sl * (size_t)Nk * D;
+    const uint16_t *__restrict__ Qp = p.Q + q_base;
+    const uint16_t *__restrict__ Kp = p.K + kv_base;
+    const uint16_t *__restrict__ Vp = p.V + kv_base;
 
-    int Lk = N;
+    int Lk = Nk;
     if (p.key_len != nullptr) {
         const int v = p.key_len[b];
-        Lk = v < 0 ? 0 : (v > N ? N : v);
+        Lk = v < 0 ? 0 : (v > Nk ? Nk : v);
     }
     const int q0 = qt * kSBM;
-    int kv_end = Lk;
-    if (CAUSAL) kv_end = min(kv_end, q0 + kSBM);
-    const int n = (kv_end + kBN - 1) / kBN;       // key tiles of the workgroup (<= NT)
     const int qw0 = q0 + wave * kQRows;           // this wave's 32 query rows
     const int my_q = qw0 + l32;
+    // causal: keys up to the highest position of the workgroup's (or the
+    // wave's) rows; tiles past the lowest position of a wave's rows need
+    // per-element masking
+    const CausalRows cr{p.Nq, p.causal_off};
+    int kv_end = Lk;
+    int wave_lo = 0, wave_hi = 0;
+    if (CAUSAL) {
+        int lo, hi;
+        cr.range(q0, min(q0 + kSBM, M) - 1, lo, hi);
+        kv_end = max(0, min(kv_end, hi + 1));
+        if (qw0 < M) cr.range(qw0, min(qw0 + kQRows, M) - 1, wave_lo, wave_hi);
+    }
+    const int my_pos = CAUSAL ? cr.pos(my_q) : 0;
+    const int n = (kv_end + kBN - 1) / kBN;       // key tiles of the workgroup (<= NT)
     int n_w = n;                                  // key tiles this wave computes
-    if (CAUSAL) n_w = (min(kv_end, qw0 + kQRows) + kBN - 1) / kBN;
-    if (qw0 >= N) n_w = 0;
+    if (CAUSAL) n_w = (max(0, min(kv_end, wave_hi + 1)) + kBN - 1) / kBN;
+    if (qw0 >= M) n_w = 0;
 
     // ---- loads: Q fragments to VGPRs (B operand of S^T: query row my_q,
-    // dims 16 kk + 8 g .. +7; rows past N are zero), K and V tiles to LDS
+    // dims 16 kk + 8 g .. +7; rows past M are zero), K and V tiles to LDS
     // (same swizzled layout as the long-sequence kernel: load instruction t
     // of a tile fills LDS bytes [1024 t, 1024 t + 1024), lane i physical
     // chunk 64 t + i).  Of a tile's 2 TILE_INSTR loads (K, then V) wave w
@@ -103,7 +117,7 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     u32x4 qreg[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk)
-        qreg[kk] = my_q < N ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + (2 * kk + g) * 8)
+        qreg[kk] = my_q < M ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + (2 * kk + g) * 8)
                             : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -161,13 +175,13 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
                 s[kb] = mfma32<BF16>(frag_k<D>(kt, kb, kk, l32, g), qreg[kk], s[kb]);
         // mask the tiles that straddle the key-length or causal limit
         const int j0 = j * kBN;
-        if ((j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > qw0)) {
+        if ((j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > wave_lo)) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool ok = key < Lk && (!CAUSAL || key <= my_q);
+                    const bool ok = key < Lk && (!CAUSAL || key <= my_pos);
                     s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
         }
@@ -199,8 +213,8 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     const Halves lh = both_halves(l_run);
     const float l_tot = lh.lo + lh.hi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_q < N) {
-        uint16_t *orow = p.O + base + (size_t)my_q * D;
+    if (my_q < M) {
+        uint16_t *orow = p.O + q_base + (size_t)my_q * D;
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
@@ -210,7 +224,7 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
                 *reinterpret_cast<u32x2 *>(orow + cb * 32 + a * 8 + g * 4) = w;
             }
         if (p.LSE != nullptr && g == 0)
-            p.LSE[(size_t)bh * N + my_q] =
+            p.LSE[(size_t)sl * M + my_q] =
                 l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
@@ -269,9 +283,9 @@ const char *fwd_short_kernel_name(bool bf16, int d, bool causal) {
 }
 
 hipError_t launch_fwd_short(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
-    if (p.N > fwd_short_max_keys(d)) return hipErrorInvalidValue;
-    p.n_qtiles = (int)((p.N + kSBM - 1) / kSBM);
-    const int64_t blocks = (int64_t)p.n_qtiles * p.BH;
+    if (p.Nk > fwd_short_max_keys(d)) return hipErrorInvalidValue;
+    p.n_qtiles = (int)((p.M + kSBM - 1) / kSBM);
+    const int64_t blocks = (int64_t)p.n_qtiles * p.slices;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(short_entry(bf16, d, causal).fn, dim3((unsigned)blocks),

@@ -10,26 +10,38 @@ namespace attn {
 
 // Arguments of one fused forward launch.  All pointers are device pointers;
 // 16-bit tensors are passed as raw bit patterns.
+//
+// Q and O are [B, H, Nq, d], K and V [B, Hkv, Nk, d], and query head h reads
+// key/value head h / (H / Hkv).  The H / Hkv query heads that share a
+// key/value head are consecutive, so their rows form one contiguous block of
+// M = (H / Hkv) * Nq rows of Q, O and LSE: a kernel works on slices
+// (b, key/value head), each M query rows against Nk keys.  Row r of a slice
+// is query r mod Nq of its head; with a causal mask it sees keys
+// j <= r mod Nq + causal_off (causal_off = Nk - Nq: the last query row is
+// aligned with the last key).  Self-attention is M = Nq = Nk, slices = B*H.
 struct FwdParams {
-    const uint16_t *Q, *K, *V;  // [B, H, N, d]
-    uint16_t *O;                // [B, H, N, d]
-    float *LSE;                 // [B, H, N] or nullptr
-    const int32_t *key_len;     // [B] or nullptr
-    int64_t N;
-    int BH;                     // B * H
-    int H;
-    int n_qtiles;               // ceil(N / query rows per workgroup)
+    const uint16_t *Q, *K, *V;
+    uint16_t *O;
+    float *LSE;                 // [B, H, Nq] or nullptr
+    const int32_t *key_len;     // [B] or nullptr: valid keys of sequence b
+    int64_t M;                  // query rows per slice
+    int64_t Nk;                 // keys per slice
+    int Nq;                     // query rows per head
+    int causal_off;             // Nk - Nq
+    int slices;                 // B * Hkv
+    int Hkv;
+    int n_qtiles;               // ceil(M / query rows per workgroup)
     float scale_log2;           // scale * log2(e), > 0
     // Key-range split (attn_fwd_splitkv): workgroup slice s covers key tiles
     // [s * split_tiles, (s + 1) * split_tiles) and writes its normalised
     // partial output and LSE, in fp32, to part_O / part_LSE.
     int kv_splits;              // 1: no split
     int split_tiles;            // 64-key tiles per split
-    float *part_O;              // [kv_splits][B*H][N][d]
-    float *part_LSE;            // [kv_splits][B*H][N]
+    float *part_O;              // [kv_splits][slices][M][d]
+    float *part_LSE;            // [kv_splits][slices][M]
 };
 
-// Streaming kernel (any N): 8 waves, 256 query rows per workgroup, K/V
+// Streaming kernel (any Nk): 8 waves, 256 query rows per workgroup, K/V
 // tiles through LDS rings, matrix-core and softmax phases ping-ponging
 // between two wave groups.  p.n_qtiles is filled in here.
 hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
@@ -44,16 +56,16 @@ const char *fwd_split_kernel_name(bool bf16, int d, bool causal);
 int fwd_split_resident_workgroups(bool bf16, int d, bool causal);
 int fwd_query_rows_per_item();
 
-// Short-sequence kernel (N <= fwd_short_max_keys(d)): 4 waves, 128 query
-// rows per workgroup, the head's whole K and V resident in LDS.
+// Short-sequence kernel (Nk <= fwd_short_max_keys(d)): 4 waves, 128 query
+// rows per workgroup, the slice's whole K and V resident in LDS.
 int64_t fwd_short_max_keys(int d);
 hipError_t launch_fwd_short(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
 const char *fwd_short_kernel_name(bool bf16, int d, bool causal);
 
-// Dispatch on (dtype, d, N, causal): the kernel attn_fwd launches, and its
+// Dispatch on (dtype, d, Nk, causal): the kernel attn_fwd launches, and its
 // name as profilers report it.
 hipError_t launch_fwd(bool bf16, int d, bool causal, FwdParams p, hipStream_t s);
-const char *fwd_kernel_name(bool bf16, int d, bool causal, int64_t N);
+const char *fwd_kernel_name(bool bf16, int d, bool causal, int64_t Nk);
 
 // Arguments of the unfused baseline, for heads [bh0, bh0 + nbh).
 struct NaiveParams {

@@ -21,6 +21,19 @@
  *   LSE_i = log(sum_j exp(S_ij)),  O_i = sum_j exp(S_ij - LSE_i) v_j.
  * A row with no visible key gets O_i = 0 and LSE_i = -inf.
  *
+ * The attn_fwd_gqa* entry points take the general shapes: Q and O
+ * [B, H, Nq, d], K and V [B, Hkv, Nk, d], H a multiple of Hkv.  Query head h
+ * reads key/value head h / (H / Hkv) (consecutive query heads share one:
+ * grouped-query attention; Hkv = 1 is multi-query attention), and queries and
+ * keys may differ in length (cross-attention, or new queries against a longer
+ * key/value history).  "cuda-reranker" lists cross-attention and
+ * grouped-query attention as extensions without defining them; these are the
+ * usual readings.  Causal masking is then aligned at the end: key j is
+ * visible to query i only when j <= i + (Nk - Nq), so the last query sees
+ * every key; with Nq = Nk this is the j <= i above, and rows with
+ * i < Nq - Nk see no key.  The self-attention entry points are the case
+ * Hkv = H, Nq = Nk = N.
+ *
  * Conventions common to all entry points
  * --------------------------------------
  *  dtype    ATTN_F16 (IEEE binary16) or ATTN_BF16 (bfloat16) for Q, K, V and
@@ -30,7 +43,9 @@
  *           16-byte aligned.  LSE: contiguous fp32 [B, H, N] device array,
  *           4-byte aligned, or NULL when not wanted.
  *  sizes    B, H, N >= 0; d in {32, 64, 128}.  B*H*N == 0 is a no-op.
- *           B*H <= 2^31 - 1 and N <= 2^30.
+ *           B*H <= 2^31 - 1 and N <= 2^30.  General shapes: Nq, Nk <= 2^30,
+ *           (H / Hkv) * Nq <= 2^30; B*H*Nq == 0 is a no-op, and Nk == 0
+ *           gives every row O = 0, LSE = -inf (K and V may then be NULL).
  *  scale    finite and >= 0 (normally 1/sqrt(d)).
  *  key_len  NULL (no padding mask) or a device int32 array [B]; values are
  *           clamped to [0, N] on the device.  K and V rows j >= L_b are never
@@ -67,7 +82,7 @@ typedef enum {
     ATTN_ERR_INVALID_ARG = 1,  /* bad size, scale, pointer or aliasing */
     ATTN_ERR_UNSUPPORTED = 2,  /* d not in {32, 64, 128} or unknown dtype */
     ATTN_ERR_MISALIGNED = 3,   /* a pointer is not aligned as required */
-    ATTN_ERR_WORKSPACE = 4,    /* naive workspace missing or too small */
+    ATTN_ERR_WORKSPACE = 4,    /* workspace missing or too small */
     ATTN_ERR_LAUNCH = 5,       /* the HIP runtime rejected a launch */
     ATTN_ERR_DEVICE = 6        /* no usable gfx950 device is current */
 } attn_status_t;
@@ -94,6 +109,25 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
                        int64_t B, int64_t H, int64_t N, int64_t d,
                        float scale, int causal, const int32_t *key_len,
                        void *stream);
+
+/*
+ * attn_fwd_gqa -- attn_fwd for the general shapes (see the top of this
+ * file): Q [B, H, Nq, d], K and V [B, Hkv, Nk, d], O [B, H, Nq, d], LSE
+ * [B, H, Nq] or NULL, key_len [B] (clamped to [0, Nk]) or NULL.
+ *
+ * One kernel launch.  A workgroup takes query rows of the H / Hkv heads that
+ * share a key/value head together (their rows are contiguous in Q and O), so
+ * each key/value tile it streams serves all of them.  Returns
+ * ATTN_ERR_INVALID_ARG when Hkv does not divide H (or Hkv is 0 with H > 0),
+ * otherwise as attn_fwd.  attn_fwd(..., N, ...) is
+ * attn_fwd_gqa(..., H, N, N, ...).
+ */
+attn_status_t attn_fwd_gqa(attn_dtype_t dtype,
+                           const void *Q, const void *K, const void *V,
+                           void *O, float *LSE,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                           int64_t d, float scale, int causal, const int32_t *key_len,
+                           void *stream);
 
 /*
  * attn_fwd_naive -- unfused baseline that materialises scores and
@@ -152,8 +186,24 @@ attn_status_t attn_fwd_splitkv(attn_dtype_t dtype,
                                int64_t n_splits, void *workspace, size_t workspace_bytes,
                                void *stream);
 
-/* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * N * (d + 1) * 4.
- * Returns 0 for sizes out of range or on overflow. */
+/*
+ * attn_fwd_gqa_splitkv -- attn_fwd_splitkv for the general shapes of
+ * attn_fwd_gqa: the key range [0, Nk) is cut into up to n_splits runs of
+ * whole 64-key tiles.  The workspace must hold
+ * attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits) bytes (the
+ * partials are per query row).  Errors as attn_fwd_gqa and attn_fwd_splitkv.
+ */
+attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype,
+                                   const void *Q, const void *K, const void *V,
+                                   void *O, float *LSE,
+                                   int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                   int64_t d, float scale, int causal, const int32_t *key_len,
+                                   int64_t n_splits, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * N * (d + 1) * 4
+ * (N = Nq for attn_fwd_gqa_splitkv).  Returns 0 for sizes out of range or on
+ * overflow. */
 size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
                                         int64_t n_splits);
 
@@ -164,12 +214,22 @@ size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t
 int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
                                         int64_t d, int causal);
 
+/* The same for the general shapes of attn_fwd_gqa_splitkv: the work items
+ * are 256-row tiles of the (H / Hkv) * Nq query rows of each of the B * Hkv
+ * key/value heads, and a split keeps at least two of the Nk keys' tiles.
+ * Returns 1 on any error. */
+int64_t attn_fwd_gqa_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H,
+                                            int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                            int causal);
+
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(attn_status_t status);
 
 /*
  * Name of the kernel instance attn_fwd launches for these arguments (for
- * profilers), written into buf (NUL-terminated, truncated to buf_len).
+ * profilers), written into buf (NUL-terminated, truncated to buf_len).  N is
+ * the key length (Nk for attn_fwd_gqa, which chooses its kernel the same
+ * way).
  * Returns the same status attn_fwd would return for an argument error,
  * else ATTN_OK.  Touches no device state.
  */

@@ -95,12 +95,44 @@ def run_split(case: dict, causal: bool, n_splits=None, inputs=None):
     return from_dev(o, case["dtype"]), lse.cpu().numpy(), n_splits
 
 
+def run_gqa(case: dict, causal: bool, inputs=None):
+    """attn_fwd_gqa: q, o [B, H, Nq, d]; k, v [B, Hkv, Nk, d]."""
+    import exact_self_attention_amd as attn
+    q, k, v, kl = inputs if inputs is not None else dev_inputs(case)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn.attn_fwd_gqa(q, k, v, o, lse, scale=float(case["scale"]), causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return from_dev(o, case["dtype"]), lse.cpu().numpy()
+
+
+def run_gqa_split(case: dict, causal: bool, n_splits=None, inputs=None):
+    """attn_fwd_gqa_splitkv with n_splits key ranges (None: the library's default)."""
+    import exact_self_attention_amd as attn
+    q, k, v, kl = inputs if inputs is not None else dev_inputs(case)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if n_splits is None:
+        code = attn.ATTN_F16 if case["dtype"] == "f16" else attn.ATTN_BF16
+        n_splits = attn.attn_fwd_gqa_splitkv_default_splits(code, B, H, Hkv, Nq, Nk, d, causal)
+    nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits)
+    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn.attn_fwd_gqa_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
+                              scale=float(case["scale"]), causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    del ws
+    return from_dev(o, case["dtype"]), lse.cpu().numpy(), n_splits
+
+
 def oracle_rows(case: dict, causal: bool, sel: np.ndarray):
+    """The oracle on rows sel; K and V may have their own [B, Hkv, Nk, d] shape."""
     dt = case["dtype"]
     Q = ai.bits_to_f32(case["Q"], dt)
     K = ai.bits_to_f32(case["K"], dt)
     V = ai.bits_to_f32(case["V"], dt)
-    return oracle.sdpa_rows(Q, K, V, float(case["scale"]), causal, case.get("key_len"), sel)
+    return oracle.attn_rows(Q, K, V, float(case["scale"]), causal, case.get("key_len"), sel)
 
 
 def sample_rows(B: int, H: int, N: int, per_head: int, seed: int) -> np.ndarray:

@@ -14,8 +14,8 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def lib():
     so = os.path.join(ROOT, "exact_self_attention_amd", "libattn.so")
     if not os.path.exists(so):
-        from exact_self_attention_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__.build()
     import exact_self_attention_amd as m
     return m
 
@@ -173,3 +173,57 @@ def test_splitkv_default_splits_without_device(lib):
     # no usable device here (or a bad argument): the default is 1 split
     assert lib.attn_fwd_splitkv_default_splits(0, 1, 4, 4096, 128, False) >= 1
     assert lib.attn_fwd_splitkv_default_splits(0, 1, 4, 4096, 48, False) == 1
+
+
+def call_gqa(lib, **kw):
+    a = dict(dtype=0, Q=A, K=A + 64 * MB, V=A + 128 * MB, O=A + 192 * MB, LSE=None,
+             B=1, H=8, Hkv=2, Nq=64, Nk=128, d=64, scale=0.125, causal=0, key_len=None)
+    a.update(kw)
+    return lib.lib.attn_fwd_gqa(a["dtype"], a["Q"], a["K"], a["V"], a["O"], a["LSE"],
+                                a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                a["scale"], a["causal"], a["key_len"], None)
+
+
+DEVICE = 6
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=3), INVALID), (dict(Hkv=0), INVALID), (dict(Hkv=16), INVALID),
+    (dict(Hkv=-1), INVALID), (dict(Nq=-1), INVALID), (dict(Nk=-1), INVALID),
+    (dict(Nk=(1 << 30) + 1), INVALID),
+    (dict(Hkv=1, Nq=(1 << 27) + 1), INVALID),         # 8 heads x Nq rows per slice > 2^30
+    (dict(d=96), UNSUPPORTED),
+    (dict(K=None), INVALID),
+    (dict(O=A + 64 * MB + 4096), INVALID),             # O overlaps K
+    (dict(LSE=A + 128 * MB), INVALID),                 # LSE overlaps V
+    (dict(K=A + 64 * MB + 8), MISALIGNED),
+])
+def test_gqa_rejects_bad_arguments(lib, kw, code):
+    assert call_gqa(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0, Hkv=0), dict(Nq=0),
+                                dict(Nq=0, Q=None, K=None, V=None, O=None)])
+def test_gqa_empty_problem_is_a_noop(lib, kw):
+    assert call_gqa(lib, **kw) == 0
+
+
+def test_gqa_accepts_what_it_should(lib):
+    # these get past every argument check; without a device the call then
+    # stops at the device check (on a GPU host it would launch)
+    ok_or_device = (0, DEVICE)
+    assert call_gqa(lib, Nk=0, K=None, V=None) in ok_or_device   # no keys: rows get O = 0
+    assert call_gqa(lib, Hkv=8) in ok_or_device                  # plain multi-head
+    assert call_gqa(lib, Hkv=1) in ok_or_device                  # one key/value head
+    assert call_gqa(lib, Nq=1, Nk=100000) in ok_or_device        # one query row
+
+
+def test_gqa_split_and_default_splits_without_device(lib):
+    a = (0, A, A + 64 * MB, A + 128 * MB, A + 192 * MB, None, 1, 8, 3, 64, 128, 64, 0.125, 0, None)
+    assert lib.lib.attn_fwd_gqa_splitkv(*a, 2, A + 256 * MB, 1 << 20, None) == INVALID  # Hkv=3
+    a = (0, A, A + 64 * MB, A + 128 * MB, A + 192 * MB, None, 1, 8, 2, 64, 128, 64, 0.125, 0, None)
+    need = lib.attn_fwd_splitkv_workspace_bytes(1, 8, 64, 64, 2)
+    assert lib.lib.attn_fwd_gqa_splitkv(*a, 2, A + 256 * MB, need - 1, None) == WORKSPACE
+    assert lib.lib.attn_fwd_gqa_splitkv(*a, 0, A + 256 * MB, need, None) == INVALID
+    assert lib.attn_fwd_gqa_splitkv_default_splits(0, 1, 8, 3, 1, 4096, 128, True) == 1
+    assert lib.attn_fwd_gqa_splitkv_default_splits(0, 1, 8, 2, 1, 4096, 128, True) >= 1

@@ -273,3 +273,106 @@ def test_prefill_shard_workload_fused_and_split():
     gu.log(f"prefill_shard8 default splits: {S}")
     Og, Lg = gu.gather(O, LSE, sel)
     gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"prefill_shard8 split S={S}", sel)
+
+
+# Grouped-query and cross-attention through attn_fwd_gqa: K and V have Hkv
+# heads and Nk rows, Q has H heads of Nq rows.  Cases: both kernels (short:
+# Nk <= 256 at d <= 64, <= 128 at d = 128), Nq < Nk and Nq > Nk (rows that
+# see no key under the end-aligned causal mask), one key/value head, single
+# query rows, slices whose 32-row wave blocks span several heads (Nq = 20,
+# 5), key lengths full / 1 / short, and Nk = 0.  Every row is checked.
+GQA_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, causal, dtype, key_len)
+    (2, 8, 2, 300, 1000, 64, True, ai.F16, None),
+    (2, 8, 2, 300, 1000, 64, False, ai.BF16, [1000, 517]),
+    (1, 6, 1, 700, 300, 128, True, ai.F16, None),
+    (3, 16, 4, 1, 2000, 128, True, ai.BF16, [2000, 1, 1234]),
+    (2, 12, 3, 20, 700, 32, True, ai.F16, [700, 650]),
+    (2, 8, 8, 513, 257, 64, True, ai.BF16, None),
+    (2, 6, 3, 77, 200, 32, True, ai.F16, None),
+    (2, 4, 2, 5, 128, 128, True, ai.BF16, [128, 60]),
+    (1, 4, 4, 33, 250, 64, False, ai.F16, None),
+    (2, 6, 2, 300, 64, 64, True, ai.F16, [64, 0]),
+    (1, 8, 2, 64, 0, 64, True, ai.F16, None),
+]
+
+
+def _gqa_id(c):
+    B, H, Hkv, Nq, Nk, d, causal, dtype, kl = c
+    return f"B{B}H{H}kv{Hkv}q{Nq}k{Nk}d{d}{'c' if causal else 'f'}{dtype}{'' if kl is None else 'L'}"
+
+
+def _gqa_case(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, salt):
+    seed = salt + B + H + Hkv + Nq + Nk + d + causal
+    return ai.random_case_general(B, H, Hkv, Nq, Nk, d, dtype, seed=seed, sigma=1.5, key_len=kl)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal,dtype,kl", GQA_CASES, ids=[_gqa_id(c) for c in GQA_CASES])
+def test_gqa_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, dtype, kl):
+    case = _gqa_case(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, 40_000)
+    gu.log(f"gqa {_gqa_id((B, H, Hkv, Nq, Nk, d, causal, dtype, kl))} key_len={kl}")
+    O, LSE = gu.run_gqa(case, causal)
+    sel = ai.all_rows_selection(B, H, Nq)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"gqa {_gqa_id((B, H, Hkv, Nq, Nk, d, causal, dtype, kl))}", sel)
+    if causal and Nq > Nk:  # rows before the first key see nothing
+        assert np.all(O[:, :, :Nq - Nk] == 0) and np.all(np.isneginf(LSE[:, :, :Nq - Nk]))
+
+
+GQA_SPLIT_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, causal, dtype, key_len, n_splits)
+    (3, 16, 4, 1, 2000, 128, True, ai.BF16, [2000, 1, 1234], 8),
+    (2, 8, 2, 300, 1000, 64, True, ai.F16, None, 3),
+    (1, 6, 1, 700, 300, 128, True, ai.F16, None, 4),
+    (2, 12, 3, 20, 700, 32, True, ai.BF16, [700, 650], 5),
+    (2, 8, 8, 1, 600, 64, False, ai.F16, [600, 0], 64),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal,dtype,kl,S", GQA_SPLIT_CASES,
+                         ids=[_gqa_id(c[:9]) + f"S{c[9]}" for c in GQA_SPLIT_CASES])
+def test_gqa_splitkv_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, S):
+    case = _gqa_case(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, 50_000)
+    gu.log(f"gqa splitkv {_gqa_id((B, H, Hkv, Nq, Nk, d, causal, dtype, kl))} S={S}")
+    O, LSE, _ = gu.run_gqa_split(case, causal, S)
+    sel = ai.all_rows_selection(B, H, Nq)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"gqa splitkv S={S}", sel)
+
+
+def test_gqa_equals_attn_fwd_on_repeated_heads():
+    # the same problem through attn_fwd with each key/value head copied to its
+    # query heads: bitwise equal (same kernel, same key order per row)
+    B, H, Hkv, N, d = 2, 8, 2, 600, 64
+    case = ai.random_case_general(B, H, Hkv, N, N, d, ai.F16, seed=41_000, key_len=[600, 333])
+    q, k, v, kl = gu.dev_inputs(case)
+    O1, L1 = gu.run_gqa(case, True, inputs=(q, k, v, kl))
+    kr = torch.repeat_interleave(k, H // Hkv, dim=1).contiguous()
+    vr = torch.repeat_interleave(v, H // Hkv, dim=1).contiguous()
+    O2, L2 = gu.run_fused(case, True, inputs=(q, kr, vr, kl))
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+GQA_ROWS_PER_HEAD = {"gqa_prefill": 32, "gqa_decode": None, "cross": 32}
+
+
+@pytest.mark.parametrize("name", ["gqa_prefill", "gqa_decode", "cross"])
+def test_gqa_workload_matches_oracle(cases, name):
+    # the full-size grouped-query / cross-attention workloads, through
+    # attn_fwd_gqa and through its split form with the default split count
+    w = ai.WORKLOADS[name]
+    case = _case(cases, name)
+    per_head = GQA_ROWS_PER_HEAD[name]
+    sel = ai.all_rows_selection(w.B, w.H, w.q_len) if per_head is None else \
+        gu.sample_rows(w.B, w.H, w.q_len, per_head, seed=w.seed + 7)
+    O_ref, LSE_ref = gu.oracle_rows(case, w.causal, sel)
+    gu.log(f"{name}: fused")
+    O, LSE = gu.run_gqa(case, w.causal)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"{name} fused", sel)
+    O, LSE, S = gu.run_gqa_split(case, w.causal)
+    gu.log(f"{name}: default splits {S}")
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"{name} split S={S}", sel)
