@@ -46,7 +46,7 @@ def load(path: str = _LIB, *, build_if_missing: bool = True) -> ctypes.CDLL:
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.oracle_attn_rows.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_double,
-                                     ctypes.c_int, p, p, i64, p, p]
+                                     ctypes.c_int, p, p, i64, i64, p, i64, p, p]
     lib.oracle_attn_rows.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -68,13 +68,31 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def attn_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
+def _mask_arg(mask, B, H, Nq, Nk):
+    """(array, stride_b, stride_h) for an additive mask broadcastable to
+    ``[B, H, Nq, Nk]``: shape ``[Nq, Nk]``, ``[B or 1, H or 1, Nq, Nk]``."""
+    if mask is None:
+        return None, 0, 0
+    m = np.asarray(mask, dtype=np.float32)
+    if m.ndim == 2:
+        m = m[None, None]
+    if m.ndim != 4 or m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) \
+            or m.shape[1] not in (1, H):
+        raise ValueError("mask must be [Nq, Nk] or [B|1, H|1, Nq, Nk]")
+    m = np.ascontiguousarray(m)
+    sb = m.shape[1] * Nq * Nk if m.shape[0] == B and B > 1 else 0
+    sh = Nq * Nk if m.shape[1] == H and H > 1 else 0
+    return m, sb, sh
+
+
+def attn_rows(Q, K, V, scale, causal: bool, key_len, sel, *, mask=None, lib=None):
     """Oracle attention on selected rows, general shapes.
 
     Q: float32 ``[B, H, Nq, d]``; K, V: float32 ``[B, Hkv, Nk, d]`` with H a
     multiple of Hkv (query head h reads key/value head h // (H // Hkv));
     causal visibility is j <= i + Nk - Nq.  ``key_len``: int ``[B]`` or None;
-    ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE
+    ``mask``: additive float mask ``[Nq, Nk]`` or ``[B|1, H|1, Nq, Nk]``, or
+    None; ``sel``: int64 ``[n, 3]`` of (b, h, i).  Returns (O ``[n, d]``, LSE
     ``[n]``) in float64.
     """
     lib = lib or _get()
@@ -96,23 +114,25 @@ def attn_rows(Q, K, V, scale, causal: bool, key_len, sel, *, lib=None):
         kl = np.ascontiguousarray(key_len, dtype=np.int32)
         if kl.shape != (B,):
             raise ValueError("key_len must have shape [B]")
+    m, msb, msh = _mask_arg(mask, B, H, Nq, Nk)
     rc = lib.oracle_attn_rows(_ptr(Q), _ptr(K), _ptr(V), B, H, Hkv, Nq, Nk, d,
                               float(scale), int(bool(causal)),
                               None if kl is None else _ptr(kl),
+                              None if m is None else _ptr(m), msb, msh,
                               _ptr(sel), n, _ptr(O), _ptr(LSE))
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments")
     return O, LSE
 
 
-def attn(Q, K, V, scale, causal: bool = False, key_len=None, *, lib=None):
+def attn(Q, K, V, scale, causal: bool = False, key_len=None, *, mask=None, lib=None):
     """Oracle attention on every row, general shapes: O ``[B,H,Nq,d]`` and
     LSE ``[B,H,Nq]`` (float64)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     B, H, Nq, d = Q.shape
     b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(Nq), indexing="ij")
     sel = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
-    O, LSE = attn_rows(Q, K, V, scale, causal, key_len, sel, lib=lib)
+    O, LSE = attn_rows(Q, K, V, scale, causal, key_len, sel, mask=mask, lib=lib)
     return O.reshape(B, H, Nq, d), LSE.reshape(B, H, Nq)
 
 

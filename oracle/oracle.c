@@ -38,6 +38,14 @@
  *     (top-left) when Nq = Nk;
  *   - a row with no visible key has O_i = 0 and LSE_i = -inf.
  *
+ * Additive mask (optional): S_ij = scale * (q_i . k_j) + mask_ij, the five
+ * steps of "Naive Attention Kernel" (section 1: scores, scale, add the mask,
+ * softmax, product with V), with a float mask element per (query, key).  The
+ * mask of (b, h) starts at element b * mask_sb + h * mask_sh and is row-major
+ * [Nq, Nk]; a stride of 0 shares one mask (the pages' [S, S]) across batch or
+ * heads.  An element of -inf removes its key like a structural mask; a row
+ * whose visible scores are all -inf is a row with no visible key.
+ *
  * The score row is materialised in full (one row at a time), followed by two
  * passes (max, then exponential sum), then the weighted sum of value rows.
  * Inputs are float32 arrays holding the exact widening of the fp16/bf16 bits
@@ -63,7 +71,8 @@ int oracle_max_threads(void) {
 
 /*
  * Q: [B, H, Nq, d]; K, V: [B, Hkv, Nk, d]; all row-major float32.
- * key_len: [B] or NULL.
+ * key_len: [B] or NULL.  mask: float32 additive mask or NULL, element
+ * (b, h, i, j) at b * mask_sb + h * mask_sh + i * Nk + j.
  * sel: n_sel triples (b, h, i) as int64, h a query head, i a query row.
  * O: [n_sel, d] double; LSE: [n_sel] double.
  * Returns 0, or -1 on a bad argument or a failed allocation.
@@ -71,11 +80,12 @@ int oracle_max_threads(void) {
 int oracle_attn_rows(const float *Q, const float *K, const float *V,
                      int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                      double scale, int causal, const int32_t *key_len,
+                     const float *mask, int64_t mask_sb, int64_t mask_sh,
                      const int64_t *sel, int64_t n_sel,
                      double *O, double *LSE)
 {
     if (B < 0 || H < 0 || Hkv <= 0 || H % Hkv != 0 || Nq < 0 || Nk < 0 || d <= 0 ||
-        n_sel < 0)
+        n_sel < 0 || mask_sb < 0 || mask_sh < 0)
         return -1;
     for (int64_t t = 0; t < n_sel; ++t) {
         int64_t b = sel[3 * t], h = sel[3 * t + 1], i = sel[3 * t + 2];
@@ -120,17 +130,24 @@ int oracle_attn_rows(const float *Q, const float *K, const float *V,
                 continue;
             }
 
-            /* scores S_ij = scale * q_i . k_j */
+            /* scores S_ij = scale * q_i . k_j (+ mask_ij) */
+            const float *mrow = mask == NULL ? NULL : mask + b * mask_sb + h * mask_sh + i * Nk;
             for (int64_t j = 0; j < n_vis; ++j) {
                 double dot = 0.0;
                 for (int64_t c = 0; c < d; ++c)
                     dot += (double)q[c] * (double)kb[j * d + c];
                 s[j] = scale * dot;
+                if (mrow != NULL) s[j] += (double)mrow[j];
             }
             /* pass 1: row maximum */
             double m = s[0];
             for (int64_t j = 1; j < n_vis; ++j)
                 if (s[j] > m) m = s[j];
+            if (m == -INFINITY) {  /* every visible key masked out by -inf */
+                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                LSE[t] = -INFINITY;
+                continue;
+            }
             /* pass 2: normaliser, then probabilities */
             double l = 0.0;
             for (int64_t j = 0; j < n_vis; ++j) {

@@ -314,14 +314,15 @@ def check_weighted_average(lib):
 
 
 # ------------------------------------------------------------ library restatement
-def textbook_numpy(Q, K, V, scale, causal=False, key_len=None):
+def textbook_numpy(Q, K, V, scale, causal=False, key_len=None, add_mask=None):
     """softmax(scale Q K^T + mask) V with numpy matmul/exp/sum on float64 copies.
 
     Q is [B, H, Nq, d], K and V [B, Hkv, Nk, d]: the key/value heads are
     expanded with np.repeat (consecutive query heads share one).  The mask
     is -inf above the diagonal that ends at the last query and key
     (np.tril with offset Nk - Nq; the plain lower triangle when Nq = Nk) and
-    at keys j >= key_len[b]."""
+    at keys j >= key_len[b], plus ``add_mask`` (any array that broadcasts to
+    [B, H, Nq, Nk]) added to the scaled scores."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     B, H, Nq, d = Q.shape
     G = H // K.shape[1]
@@ -329,6 +330,8 @@ def textbook_numpy(Q, K, V, scale, causal=False, key_len=None):
     V = np.repeat(V, G, axis=1)
     Nk = K.shape[2]
     S = scale * np.matmul(Q, np.swapaxes(K, -1, -2))
+    if add_mask is not None:
+        S = S + np.asarray(add_mask, np.float64)
     mask = np.zeros((B, 1, Nq, Nk))
     if causal:
         mask = mask + np.where(np.tril(np.ones((Nq, Nk)), k=Nk - Nq) > 0, 0.0, -np.inf)
@@ -391,11 +394,11 @@ def check_online_merge_matches(lib):
 
 
 # ------------------------------------------------------------ cross-attention and grouped heads
-def _run_general(lib, Q, K, V, scale, causal=False, key_len=None):
+def _run_general(lib, Q, K, V, scale, causal=False, key_len=None, mask=None):
     Q = np.asarray(Q, dtype=np.float32)
     K = np.asarray(K, dtype=np.float32)
     V = np.asarray(V, dtype=np.float32)
-    return oracle.attn(Q, K, V, scale, causal, key_len, lib=lib)
+    return oracle.attn(Q, K, V, scale, causal, key_len, mask=mask, lib=lib)
 
 
 def check_grouped_heads_equal_repeated_heads(lib):
@@ -471,6 +474,102 @@ def check_cross_zero_query_prefix_means(lib):
                     ref = V[0, hk, :n].astype(np.float64).mean(axis=0)
                     assert np.allclose(O[0, h, i], ref, rtol=0, atol=1e-14)
                     assert abs(LSE[0, h, i] - math.log(n)) < 1e-14
+
+
+# ------------------------------------------------------------ additive mask
+def check_mask_minus_inf_is_a_structural_mask(lib):
+    """An additive mask of -inf above the end-aligned diagonal equals the
+    causal flag, -inf at keys j >= L equals key_len = L, and a row whose mask
+    is -inf everywhere has no visible key (O = 0, LSE = -inf)."""
+    rng = _rng(41)
+    for Nq, Nk in ((20, 20), (7, 30), (30, 7)):
+        B, H, Hkv, d = 2, 4, 2, 8
+        Q = _randn(rng, (B, H, Nq, d), 1.5)
+        K = _randn(rng, (B, Hkv, Nk, d), 1.5)
+        V = _randn(rng, (B, Hkv, Nk, d))
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        causal_mask = np.where(j <= i + Nk - Nq, 0.0, -np.inf).astype(np.float32)
+        O1, L1 = _run_general(lib, Q, K, V, 0.4, causal=True)
+        O2, L2 = _run_general(lib, Q, K, V, 0.4, mask=causal_mask)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+        kl = np.array([Nk, max(Nk // 3, 1)], np.int32)
+        pad = np.broadcast_to(np.where(np.arange(Nk)[None, :] < kl[:, None], 0.0, -np.inf)
+                              [:, None, None, :], (B, 1, Nq, Nk)).astype(np.float32)
+        O1, L1 = _run_general(lib, Q, K, V, 0.4, key_len=kl)
+        O2, L2 = _run_general(lib, Q, K, V, 0.4, mask=pad)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    m = np.zeros((Nq, Nk), np.float32)
+    m[3, :] = -np.inf
+    O, L = _run_general(lib, Q, K, V, 0.4, mask=m)
+    assert np.all(O[:, :, 3] == 0.0) and np.all(np.isneginf(L[:, :, 3]))
+    assert np.all(np.isfinite(L[:, :, :3]))
+
+
+def check_mask_log_weights_closed_form(lib):
+    """Q = 0 and mask = log w: the weights are w_ij / sum_j w_ij, so
+    O_i = sum_j w_ij v_j / sum_j w_ij and LSE_i = log sum_j w_ij.  A
+    different, non-symmetric w per (b, h) pins the mask's indexing."""
+    rng = _rng(42)
+    B, H, Hkv, Nq, Nk, d = 2, 3, 3, 5, 9, 4
+    Q = np.zeros((B, H, Nq, d), np.float32)
+    K = _randn(rng, (B, Hkv, Nk, d))
+    V = _randn(rng, (B, Hkv, Nk, d))
+    W = rng.uniform(0.05, 3.0, size=(B, H, Nq, Nk))
+    mask = np.log(W).astype(np.float32)
+    W = np.exp(mask.astype(np.float64))  # the weights the float32 mask encodes
+    O, LSE = _run_general(lib, Q, K, V, 0.9, mask=mask)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                w = W[b, h, i]
+                ref = (w[:, None] * V[b, h].astype(np.float64)).sum(axis=0) / w.sum()
+                assert np.allclose(O[b, h, i], ref, rtol=1e-13, atol=1e-13)
+                assert abs(LSE[b, h, i] - math.log(w.sum())) < 1e-13
+
+
+def check_mask_textbook_numpy(lib):
+    """A random finite mask, with and without the structural masks and
+    grouped heads, against numpy."""
+    rng = _rng(43)
+    for (B, H, Hkv, Nq, Nk, d, causal, kl, mshape) in [
+            (1, 2, 2, 9, 9, 8, False, None, (9, 9)),
+            (2, 4, 2, 6, 13, 16, True, [13, 4], (2, 4, 6, 13)),
+            (2, 3, 1, 11, 5, 8, True, None, (1, 3, 11, 5)),
+            (3, 2, 2, 8, 8, 32, False, [8, 0, 3], (3, 1, 8, 8))]:
+        Q = _randn(rng, (B, H, Nq, d), 1.5)
+        K = _randn(rng, (B, Hkv, Nk, d), 1.5)
+        V = _randn(rng, (B, Hkv, Nk, d))
+        m = _randn(rng, mshape, 2.0)
+        key_len = None if kl is None else np.array(kl, np.int32)
+        O, LSE = _run_general(lib, Q, K, V, 0.37, causal, key_len, mask=m)
+        Oref, LSEref = textbook_numpy(Q, K, V, 0.37, causal, key_len, add_mask=m)
+        assert np.allclose(O, Oref, rtol=1e-12, atol=1e-12)
+        fin = np.isfinite(LSEref)
+        assert np.array_equal(fin, np.isfinite(LSE))
+        assert np.allclose(LSE[fin], LSEref[fin], rtol=1e-12, atol=1e-12)
+
+
+def check_mask_broadcast_equals_copies(lib):
+    """A shared [Nq, Nk] mask (strides 0) equals the same mask copied to every
+    (b, h), and a per-row constant added to the mask moves LSE by it and
+    leaves O unchanged."""
+    rng = _rng(44)
+    B, H, Hkv, Nq, Nk, d = 2, 4, 2, 7, 12, 8
+    Q = _randn(rng, (B, H, Nq, d))
+    K = _randn(rng, (B, Hkv, Nk, d))
+    V = _randn(rng, (B, Hkv, Nk, d))
+    m = (np.round(_randn(rng, (Nq, Nk)) * 256.0) / 256.0).astype(np.float32)  # m + c exact
+    O1, L1 = _run_general(lib, Q, K, V, 0.5, True, mask=m)
+    O2, L2 = _run_general(lib, Q, K, V, 0.5, True,
+                          mask=np.broadcast_to(m, (B, H, Nq, Nk)).copy())
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    c = (np.arange(Nq, dtype=np.float32) * 0.25 - 1.0)[:, None]
+    mc = (m + c).astype(np.float32)
+    assert np.array_equal(mc - c, m)  # the shift was exact in float32
+    O3, L3 = _run_general(lib, Q, K, V, 0.5, True, mask=mc)
+    assert np.allclose(O3, O1, rtol=1e-12, atol=1e-12)
+    assert np.allclose(L3, L1 + c[:, 0], rtol=0, atol=1e-12)
 
 
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

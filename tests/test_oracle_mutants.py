@@ -28,6 +28,16 @@ MUTANTS = {
     "query_head_from_kv_head": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
                                 "const float *q  = Q + ((b * H + hk) * Nq + i) * d;"),
     "key_len_ignored": ("L = key_len[b];", "L = Nk;"),
+    "mask_ignored": ("if (mrow != NULL) s[j] += (double)mrow[j];", ""),
+    "mask_scaled": ("if (mrow != NULL) s[j] += (double)mrow[j];",
+                    "if (mrow != NULL) s[j] += scale * (double)mrow[j];"),
+    "mask_sign": ("if (mrow != NULL) s[j] += (double)mrow[j];",
+                  "if (mrow != NULL) s[j] -= (double)mrow[j];"),
+    "mask_first_row_only": ("+ h * mask_sh + i * Nk;", "+ h * mask_sh + 0 * Nk;"),
+    "mask_batch_ignored": ("mask + b * mask_sb + h * mask_sh", "mask + h * mask_sh"),
+    "mask_head_ignored": ("mask + b * mask_sb + h * mask_sh", "mask + b * mask_sb"),
+    "masked_row_not_empty": ("if (m == -INFINITY) {  /* every visible key masked out by -inf */",
+                             "if (0) {"),
     "key_operand_for_query": ("dot += (double)q[c] * (double)kb[j * d + c];",
                               "dot += (double)kb[j * d + c] * (double)kb[j * d + c];"),
     "key_operand_for_value": ("o[c] += p[j] * (double)vb[j * d + c];",
@@ -38,7 +48,8 @@ MUTANTS = {
     "lse_log2": ("LSE[t] = m + log(l);", "LSE[t] = m + log2(l);"),
     "min_for_max": ("if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
     "dot_offset": ("double dot = 0.0;", "double dot = 1.0;"),
-    "empty_row_lse_zero": ("LSE[t] = -INFINITY;", "LSE[t] = 0.0;"),
+    "empty_row_lse_zero": ("if (n_vis == 0) {\n                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;\n                LSE[t] = -INFINITY;",
+                           "if (n_vis == 0) {\n                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;\n                LSE[t] = 0.0;"),
     "value_row_skipped": ("for (int64_t j = 0; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +=",
                           "for (int64_t j = 1; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +="),
     "query_row_off_by_one": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
