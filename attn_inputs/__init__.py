@@ -49,6 +49,13 @@ extensions; the pages give no shapes for them, so these reuse theirs:
   fp16, no mask.
 
 Draw order for these is Q, K, V with their own shapes, then key lengths.
+
+One measures the additive score mask of "Naive Attention Kernel" (a float
+[S, S] mask added to the scaled scores):
+
+* ``masked_prefill``: the prefill (B=1 H=32 N=4096 d=128 fp16, causal) with
+  one fp32 [4096, 4096] mask shared by all heads, drawn N(0, 1) after Q, K
+  and V (a dense additive bias on top of the causal structure).
 """
 from __future__ import annotations
 
@@ -80,6 +87,7 @@ class Workload:
     sample_rows: Optional[int] = None  # query rows per head the oracle checks
     Hkv: Optional[int] = None  # key/value heads (None: H)
     Nq: Optional[int] = None   # query rows per head (None: N, the key length)
+    mask_sigma: Optional[float] = None  # shared fp32 [Nq, N] additive mask ~ N(0, sigma^2)
 
     @property
     def scale(self) -> np.float32:
@@ -127,10 +135,13 @@ WORKLOADS = {
     "gqa_decode": Workload("gqa_decode", 8, 32, 32768, 128, BF16, True, True,
                            key_len_lo=16384, key_len_hi=32768, seed=1008, Hkv=8, Nq=1),
     "cross": Workload("cross", 4, 16, 4096, 64, F16, False, False, seed=1009, Nq=2048),
+    # additive score mask
+    "masked_prefill": Workload("masked_prefill", 1, 32, 4096, 128, F16, True, False, seed=1010,
+                               mask_sigma=1.0),
 }
 WORKLOAD_ORDER = ["single_head", "reranker", "prefill", "peaky", "long_context"]
 # workloads beyond the five the pages' configurations describe
-EXTRA_WORKLOADS = ["prefill_shard8", "gqa_prefill", "gqa_decode", "cross"]
+EXTRA_WORKLOADS = ["prefill_shard8", "gqa_prefill", "gqa_decode", "cross", "masked_prefill"]
 
 
 # ---------------------------------------------------------------- rounding
@@ -197,6 +208,9 @@ def generate(w: Workload, seed: Optional[int] = None) -> dict:
     if w.key_padding:
         out["key_len"] = rng.integers(w.key_len_lo, w.key_len_hi + 1,
                                       size=w.B).astype(np.int32)
+    out["mask"] = None
+    if w.mask_sigma is not None:
+        out["mask"] = _normal(rng, (w.q_len, w.N), w.mask_sigma)
     out["rows"] = None
     if w.sample_rows is not None:
         out["rows"] = np.stack([
@@ -238,6 +252,20 @@ def random_case_general(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, dtyp
         key_len = rng.integers(0, Nk + 1, size=B)
     out["key_len"] = None if key_len is None else np.asarray(key_len, dtype=np.int32)
     return out
+
+
+def random_mask(shape, *, seed: int, sigma: float = 1.0, neg_inf_frac: float = 0.0,
+                empty_rows=()) -> np.ndarray:
+    """An fp32 additive mask of the given shape drawn N(0, sigma^2); then a
+    fraction ``neg_inf_frac`` of its elements set to -inf, and every element
+    of the rows ``empty_rows`` (indices into the second-to-last axis) too."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = _normal(rng, shape, sigma)
+    if neg_inf_frac > 0:
+        m[rng.random(size=shape) < neg_inf_frac] = -np.inf
+    for r in empty_rows:
+        m[..., r, :] = -np.inf
+    return m
 
 
 def all_rows_selection(B: int, H: int, N: int) -> np.ndarray:

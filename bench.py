@@ -96,14 +96,18 @@ def metric_flops(w) -> float:
 
 def algorithmic_bytes(w, key_len=None) -> int:
     """Q and O once, each key/value head's visible K and V rows once, LSE once
-    (4 B per query row)."""
+    (4 B per query row), and a shared additive mask's elements that some
+    query sees once (4 B each)."""
     elem = 2
     qo = 2 * w.B * w.H * w.q_len * w.d * elem
     kv = 0
     for L in key_lengths(w, key_len):
         seen = int(visible_per_query(w, int(L)).max()) if w.q_len > 0 else 0
         kv += 2 * w.kv_heads * seen * w.d * elem
-    return qo + kv + w.B * w.H * w.q_len * 4
+    mask = 0
+    if w.mask_sigma is not None:  # one [Nq, N] mask shared by all (b, h)
+        mask = 4 * int(visible_per_query(w, int(key_lengths(w, key_len).max())).sum())
+    return qo + kv + w.B * w.H * w.q_len * 4 + mask
 
 
 def source_digest() -> str:
@@ -203,14 +207,14 @@ def cpu_baseline(w, case, target_s: float):
 
     sel = pick(min(2, w.q_len))
     t0 = time.perf_counter()
-    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel, mask=case.get("mask"))
     rate = rows_flops(sel) / max(time.perf_counter() - t0, 1e-6)
     per_row = max(1.0, 4 * w.d * float(np.mean([v.mean() for v in vis.values()])))
     per_head = int(max(1, min(w.q_len, target_s * rate / per_row / (w.B * w.H))))
     sel = pick(per_head)
     flops = rows_flops(sel)
     t0 = time.perf_counter()
-    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel)
+    oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel, mask=case.get("mask"))
     secs = time.perf_counter() - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
@@ -257,7 +261,11 @@ def main():
         ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.q_len, w.d,
                                                                n_splits) // 4,
                          dtype=torch.float32, device=dev)
-    if w.general:
+    mask = None
+    if w.mask_sigma is not None:
+        mask = torch.from_numpy(case["mask"]).to(dev)
+        entry = "attn_fwd_masked_splitkv" if use_split else "attn_fwd_masked"
+    elif w.general:
         entry = "attn_fwd_gqa_splitkv" if use_split else "attn_fwd_gqa"
     else:
         entry = "attn_fwd_splitkv" if use_split else "attn_fwd"
@@ -272,6 +280,13 @@ def main():
                                       scale=scale, causal=w.causal, key_len=kl)
         elif entry == "attn_fwd_gqa":
             attn.attn_fwd_gqa(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
+        elif entry == "attn_fwd_masked":
+            attn.attn_fwd_masked(q, k, v, o, lse, mask=mask, scale=scale, causal=w.causal,
+                                 key_len=kl)
+        elif entry == "attn_fwd_masked_splitkv":
+            attn.attn_fwd_masked_splitkv(q, k, v, o, lse, mask=mask, workspace=ws,
+                                         n_splits=n_splits, scale=scale, causal=w.causal,
+                                         key_len=kl)
         else:
             attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
 
@@ -321,8 +336,11 @@ def main():
     pairs = visible_pairs(w, key_len)
     F_alg = 4.0 * w.d * pairs
     kernel = attn.attn_fwd_kernel_name(code, w.d, w.N, w.causal, key_len is not None)
+    tail = f"d{w.d}_{w.dtype}_{'causal' if w.causal else 'full'}"
     if n_splits is not None:  # the split form always runs the streaming kernel
-        kernel = f"attn_fwd_split_d{w.d}_{w.dtype}_{'causal' if w.causal else 'full'}"
+        kernel = f"attn_fwd_split_{'mask_' if mask is not None else ''}{tail}"
+    elif mask is not None:  # and so does the masked form
+        kernel = f"attn_fwd_mask_{tail}"
     nbytes = algorithmic_bytes(w, key_len)
     # the bound: HBM when the flops per algorithmic byte are below the
     # machine balance (matrix-core peak / HBM bandwidth), else the matrix cores
@@ -350,14 +368,15 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "Hkv": w.kv_heads, "Nq": w.q_len,
+                   "mask": None if mask is None else f"fp32 [{w.q_len}, {w.N}] shared, N(0, {w.mask_sigma}^2)",
                    "causal": w.causal, "key_padding": w.key_padding, "seed": w.seed,
                    "kv_splits": n_splits,
                    "global_batch": w.B, "seq_len": w.N},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
         "roofline": roof,
     }
-    # the unfused baseline takes self-attention shapes only
-    if not args.no_naive and not w.general:
+    # the unfused baseline takes self-attention shapes without a mask only
+    if not args.no_naive and not w.general and mask is None:
         nb = naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F)
         nb["fused_speedup"] = nb["ms_per_step"] / ms_per_step
         out["naive_baseline"] = nb

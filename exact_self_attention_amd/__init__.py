@@ -28,6 +28,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
 EXPORTS = ["attn_fwd", "attn_fwd_gqa", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_gqa_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_splitkv_default_splits", "attn_fwd_gqa_splitkv_default_splits",
+           "attn_fwd_masked", "attn_fwd_masked_splitkv",
            "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
 
 
@@ -51,6 +52,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_gqa.restype = i32
     lib.attn_fwd_gqa_splitkv.argtypes = general + [i64, p, ctypes.c_size_t, p]
     lib.attn_fwd_gqa_splitkv.restype = i32
+    lib.attn_fwd_masked.argtypes = general + [p, i64, i64, p]
+    lib.attn_fwd_masked.restype = i32
+    lib.attn_fwd_masked_splitkv.argtypes = general + [p, i64, i64, i64, p, ctypes.c_size_t, p]
+    lib.attn_fwd_masked_splitkv.restype = i32
     lib.attn_fwd_gqa_splitkv_default_splits.argtypes = [i32, i64, i64, i64, i64, i64, i64, i32]
     lib.attn_fwd_gqa_splitkv_default_splits.restype = i64
     lib.attn_fwd_naive.argtypes = common + [p, ctypes.c_size_t, p]
@@ -161,6 +166,59 @@ def attn_fwd_gqa_splitkv(q, k, v, o, lse=None, *, workspace: torch.Tensor, n_spl
                                   _stream(stream, q.device))
     if st != 0:
         raise AttnError("attn_fwd_gqa_splitkv", st)
+
+
+def _mask_strides(mask, q, k):
+    """(stride_b, stride_h) in elements of an fp32 mask tensor of shape
+    [Nq, Nk] or [B|1, H|1, Nq, Nk] whose rows are contiguous (broadcast
+    views from expand() are accepted: their stride is 0)."""
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
+    if mask.dtype != torch.float32 or mask.device != q.device:
+        raise ValueError("mask must be a float32 tensor on q's device")
+    if mask.dim() == 2:
+        mask = mask.view(1, 1, *mask.shape)
+    if mask.dim() != 4 or tuple(mask.shape[2:]) != (Nq, Nk) or mask.shape[0] not in (1, B) \
+            or mask.shape[1] not in (1, H):
+        raise ValueError("mask must be [Nq, Nk] or [B|1, H|1, Nq, Nk]")
+    if (Nk > 1 and mask.stride(3) != 1) or (Nq > 1 and mask.stride(2) != Nk):
+        raise ValueError("mask rows must be contiguous [Nq, Nk] blocks")
+    sb = mask.stride(0) if mask.shape[0] == B and B > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] == H and H > 1 else 0
+    return sb, sh
+
+
+def attn_fwd_masked(q, k, v, o, lse=None, *, mask: torch.Tensor, scale: float,
+                    causal: bool = False, key_len=None, stream=None) -> None:
+    """attn_fwd_gqa with an additive fp32 score mask (see include/attn.h)."""
+    code = _dtype_code(q)
+    _check_general(q, k, v, o, lse, key_len)
+    sb, sh = _mask_strides(mask, q, k)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    st = lib.attn_fwd_masked(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                             _ptr(key_len), mask.data_ptr(), sb, sh, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_masked", st)
+
+
+def attn_fwd_masked_splitkv(q, k, v, o, lse=None, *, mask: torch.Tensor, workspace: torch.Tensor,
+                            n_splits: int, scale: float, causal: bool = False, key_len=None,
+                            stream=None) -> None:
+    """attn_fwd_masked over ``n_splits`` key ranges, merged."""
+    code = _dtype_code(q)
+    _check_general(q, k, v, o, lse, key_len)
+    sb, sh = _mask_strides(mask, q, k)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_masked_splitkv(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                     _ptr(key_len), mask.data_ptr(), sb, sh, int(n_splits),
+                                     _ptr(workspace), nbytes, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_masked_splitkv", st)
 
 
 def attn_fwd_gqa_splitkv_default_splits(dtype: int, B: int, H: int, Hkv: int, Nq: int, Nk: int,

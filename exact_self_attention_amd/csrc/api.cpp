@@ -99,12 +99,41 @@ attn::FwdParams make_params(const void *Q, const void *K, const void *V, void *O
     p.split_tiles = 0;
     p.part_O = nullptr;
     p.part_LSE = nullptr;
+    p.mask = nullptr;
+    p.mask_sb = 0;
+    p.mask_sh = 0;
+    p.mask_bytes = 0;
     // The kernel needs a positive exp2 scale (masked scores are -inf and must
     // map to exactly 0).  A zero scale becomes 1e-30: every score times it
     // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     if (!(p.scale_log2 >= 1e-30f)) p.scale_log2 = 1e-30f;
     return p;
+}
+
+// Checks of an additive mask for a checked, non-empty problem; fills the
+// mask fields of p.  Element (b, h, i, j) is at b * sb + h * sh + i * Nk + j;
+// one batch's part must stay below 2 GiB (the kernel addresses it with
+// 32-bit offsets).
+attn_status_t check_mask(const float *mask, int64_t sb, int64_t sh, const Shape &sh_, const void *O,
+                         const float *LSE, attn::FwdParams *p) {
+    if (mask == nullptr || sb < 0 || sh < 0) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(mask, 4)) return ATTN_ERR_MISALIGNED;
+    const unsigned __int128 per_batch =
+        ((unsigned __int128)(sh_.H - 1) * (unsigned __int128)sh +
+         (unsigned __int128)sh_.Nq * (unsigned __int128)sh_.Nk) * 4u;
+    if (per_batch > (unsigned __int128)(INT32_MAX - 64)) return ATTN_ERR_INVALID_ARG;
+    const unsigned __int128 total = (unsigned __int128)(sh_.B - 1) * (unsigned __int128)sb * 4u + per_batch;
+    if (total > (unsigned __int128)SIZE_MAX) return ATTN_ERR_INVALID_ARG;
+    const size_t qbytes = sh_.q_elems() * (size_t)sh_.d * 2;
+    if (overlaps(mask, (size_t)total, O, qbytes) ||
+        overlaps(mask, (size_t)total, LSE, LSE ? sh_.q_elems() * 4 : 0))
+        return ATTN_ERR_INVALID_ARG;
+    p->mask = mask;
+    p->mask_sb = sb;
+    p->mask_sh = sh;
+    p->mask_bytes = (uint32_t)per_batch;
+    return ATTN_OK;
 }
 
 // The current device must be a gfx950; checked once per device.
@@ -138,6 +167,27 @@ attn_status_t attn_fwd_gqa(attn_dtype_t dtype, const void *Q, const void *K, con
     st = check_device();
     if (st != ATTN_OK) return st;
     const attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
+    const hipError_t e = attn::launch_fwd(dtype == ATTN_BF16, (int)d, causal != 0, p,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd_masked(attn_dtype_t dtype, const void *Q, const void *K, const void *V,
+                              void *O, float *LSE, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                              int64_t Nk, int64_t d, float scale, int causal,
+                              const int32_t *key_len, const float *mask, int64_t mask_stride_b,
+                              int64_t mask_stride_h, void *stream) {
+    const Shape sh{B, H, Hkv, Nq, Nk, d};
+    bool empty = false;
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, sh, scale, key_len, &empty);
+    if (st != ATTN_OK) return st;
+    if (mask == nullptr || mask_stride_b < 0 || mask_stride_h < 0) return ATTN_ERR_INVALID_ARG;
+    if (empty) return ATTN_OK;
+    attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
+    st = check_mask(mask, mask_stride_b, mask_stride_h, sh, O, LSE, &p);
+    if (st != ATTN_OK) return st;
+    st = check_device();
+    if (st != ATTN_OK) return st;
     const hipError_t e = attn::launch_fwd(dtype == ATTN_BF16, (int)d, causal != 0, p,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -199,16 +249,21 @@ attn_status_t attn_fwd_naive(attn_dtype_t dtype, const void *Q, const void *K, c
     return ATTN_OK;
 }
 
-attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
-                                   const void *V, void *O, float *LSE, int64_t B, int64_t H,
-                                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
-                                   int causal, const int32_t *key_len, int64_t n_splits,
-                                   void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// The split-key forward, with an additive mask when `masked`.
+attn_status_t splitkv(attn_dtype_t dtype, const void *Q, const void *K, const void *V, void *O,
+                      float *LSE, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                      int64_t d, float scale, int causal, const int32_t *key_len, bool masked,
+                      const float *mask, int64_t mask_sb, int64_t mask_sh, int64_t n_splits,
+                      void *workspace, size_t workspace_bytes, void *stream) {
     const Shape sh{B, H, Hkv, Nq, Nk, d};
     bool empty = false;
     attn_status_t st = check_args(dtype, Q, K, V, O, LSE, sh, scale, key_len, &empty);
     if (st != ATTN_OK) return st;
     if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+    if (masked && (mask == nullptr || mask_sb < 0 || mask_sh < 0)) return ATTN_ERR_INVALID_ARG;
     if (empty) return ATTN_OK;
     const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits);
     if (need == 0) return ATTN_ERR_INVALID_ARG;
@@ -223,6 +278,14 @@ attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void
         overlaps(workspace, workspace_bytes, LSE, LSE ? sh.q_elems() * 4 : 0) ||
         overlaps(workspace, workspace_bytes, key_len, key_len ? (size_t)B * 4 : 0))
         return ATTN_ERR_INVALID_ARG;
+    attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
+    if (masked) {
+        st = check_mask(mask, mask_sb, mask_sh, sh, O, LSE, &p);
+        if (st != ATTN_OK) return st;
+        if (overlaps(workspace, workspace_bytes, mask,
+                     (size_t)(B - 1) * (size_t)mask_sb * 4 + p.mask_bytes))
+            return ATTN_ERR_INVALID_ARG;
+    }
     st = check_device();
     if (st != ATTN_OK) return st;
 
@@ -231,7 +294,6 @@ attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void
     const int64_t tiles = (Nk + 63) / 64;
     const int64_t per = tiles > 0 ? (tiles + n_splits - 1) / n_splits : 1;
     const int64_t used = tiles > 0 ? (tiles + per - 1) / per : 1;
-    attn::FwdParams p = make_params(Q, K, V, O, LSE, sh, scale, key_len);
     p.kv_splits = (int)used;
     p.split_tiles = (int)per;
     p.part_O = static_cast<float *>(workspace);
@@ -239,6 +301,30 @@ attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void
     const hipError_t e = attn::launch_fwd_split(dtype == ATTN_BF16, (int)d, causal != 0, p,
                                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
+                                   const void *V, void *O, float *LSE, int64_t B, int64_t H,
+                                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                   int causal, const int32_t *key_len, int64_t n_splits,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    return splitkv(dtype, Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, key_len, false,
+                   nullptr, 0, 0, n_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_fwd_masked_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
+                                      const void *V, void *O, float *LSE, int64_t B, int64_t H,
+                                      int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                      int causal, const int32_t *key_len, const float *mask,
+                                      int64_t mask_stride_b, int64_t mask_stride_h,
+                                      int64_t n_splits, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+    return splitkv(dtype, Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, key_len, true,
+                   mask, mask_stride_b, mask_stride_h, n_splits, workspace, workspace_bytes,
+                   stream);
 }
 
 attn_status_t attn_fwd_splitkv(attn_dtype_t dtype, const void *Q, const void *K, const void *V,

@@ -26,6 +26,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kQRows = 32;               // query rows per wave
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 // Lazy running max.  The running max only moves when a tile's max exceeds
 // it by more than kLazy (log2 units), and then to kHeadroom above that
 // tile's max, so that it rarely has to move again.  Probabilities stay below

@@ -1,5 +1,5 @@
 // Kernel choice for attn_fwd: the short-sequence kernel when a slice's keys
-// fit in LDS, the streaming kernel otherwise.
+// fit in LDS, the streaming kernel otherwise (and always with a mask).
 #include "kernels.h"
 
 namespace attn {
@@ -9,7 +9,7 @@ bool use_short(int d, int64_t Nk) { return Nk <= fwd_short_max_keys(d); }
 }  // namespace
 
 hipError_t launch_fwd(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
-    return use_short(d, p.Nk) ? launch_fwd_short(bf16, d, causal, p, s)
+    return use_short(d, p.Nk) && p.mask == nullptr ? launch_fwd_short(bf16, d, causal, p, s)
                              : launch_fwd_fused(bf16, d, causal, p, s);
 }
 

@@ -39,7 +39,15 @@ struct FwdParams {
     int split_tiles;            // 64-key tiles per split
     float *part_O;              // [kv_splits][slices][M][d]
     float *part_LSE;            // [kv_splits][slices][M]
+    // Additive fp32 mask (attn_fwd_masked) or nullptr: element (b, h, i, j)
+    // at b * mask_sb + h * mask_sh + i * Nk + j; mask_bytes covers one
+    // batch's part (< 2^31).
+    const float *mask;
+    int64_t mask_sb, mask_sh;
+    uint32_t mask_bytes;
 };
+
+typedef void (*FwdKernelFn)(FwdParams);
 
 // Streaming kernel (any Nk): 8 waves, 256 query rows per workgroup, K/V
 // tiles through LDS rings, matrix-core and softmax phases ping-ponging
@@ -55,6 +63,11 @@ const char *fwd_split_kernel_name(bool bf16, int d, bool causal);
 // Workgroups of the split kernel the current device holds at once (0 on error).
 int fwd_split_resident_workgroups(bool bf16, int d, bool causal);
 int fwd_query_rows_per_item();
+
+// Streaming kernel instances with the additive mask (plain or split-key);
+// launch_fwd_fused and launch_fwd_split take them when p.mask is set.
+FwdKernelFn fwd_masked_kernel(bool bf16, int d, bool causal, bool split);
+const char *fwd_masked_kernel_name(bool bf16, int d, bool causal, bool split);
 
 // Short-sequence kernel (Nk <= fwd_short_max_keys(d)): 4 waves, 128 query
 // rows per workgroup, the slice's whole K and V resident in LDS.

@@ -130,6 +130,35 @@ attn_status_t attn_fwd_gqa(attn_dtype_t dtype,
                            void *stream);
 
 /*
+ * attn_fwd_masked -- attn_fwd_gqa with an additive score mask: the scores
+ * become S_ij = scale * (q_i . k_j) + mask_ij before the softmax, the
+ * five-step form of "Naive Attention Kernel" (section 1: scores, scale, add
+ * the mask, softmax, product with V) with its float mask.
+ *
+ * mask: device fp32 array, 4-byte aligned, element (b, h, i, j) at
+ * b * mask_stride_b + h * mask_stride_h + i * Nk + j (strides in elements,
+ * >= 0; rows of one (b, h) are contiguous).  Strides of 0 share one
+ * [Nq, Nk] mask (the pages' [S, S]) across batch and heads.  One batch's
+ * part, ((H - 1) * mask_stride_h + Nq * Nk) * 4 bytes, must be below 2 GiB.
+ * An element of -inf removes that key as the structural masks do; a row all
+ * of whose visible keys are -inf gets O = 0 and LSE = -inf.  +inf or NaN
+ * elements give undefined results.  causal and key_len still apply.  The
+ * mask is read, never written; it must not overlap O or LSE.
+ *
+ * One kernel launch (the streaming kernel for every Nk).  Returns
+ * ATTN_ERR_INVALID_ARG for a NULL mask, negative strides, an oversized mask
+ * or an overlap, ATTN_ERR_MISALIGNED for a misaligned mask, otherwise as
+ * attn_fwd_gqa.
+ */
+attn_status_t attn_fwd_masked(attn_dtype_t dtype,
+                              const void *Q, const void *K, const void *V,
+                              void *O, float *LSE,
+                              int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                              int64_t d, float scale, int causal, const int32_t *key_len,
+                              const float *mask, int64_t mask_stride_b, int64_t mask_stride_h,
+                              void *stream);
+
+/*
  * attn_fwd_naive -- unfused baseline that materialises scores and
  * probabilities ("Naive Attention Kernel", sections 1 and 3; "Tensor
  * Parallelism with CUDA - Standard Attention", sections "Why This
@@ -200,6 +229,22 @@ attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype,
                                    int64_t d, float scale, int causal, const int32_t *key_len,
                                    int64_t n_splits, void *workspace, size_t workspace_bytes,
                                    void *stream);
+
+/*
+ * attn_fwd_masked_splitkv -- attn_fwd_masked over up to n_splits key
+ * ranges, merged as attn_fwd_splitkv does.  Workspace and errors as
+ * attn_fwd_gqa_splitkv and attn_fwd_masked; the workspace must not overlap
+ * the mask either.
+ */
+attn_status_t attn_fwd_masked_splitkv(attn_dtype_t dtype,
+                                      const void *Q, const void *K, const void *V,
+                                      void *O, float *LSE,
+                                      int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                      int64_t d, float scale, int causal,
+                                      const int32_t *key_len, const float *mask,
+                                      int64_t mask_stride_b, int64_t mask_stride_h,
+                                      int64_t n_splits, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * N * (d + 1) * 4
  * (N = Nq for attn_fwd_gqa_splitkv).  Returns 0 for sizes out of range or on

@@ -126,13 +126,37 @@ def run_gqa_split(case: dict, causal: bool, n_splits=None, inputs=None):
     return from_dev(o, case["dtype"]), lse.cpu().numpy(), n_splits
 
 
-def oracle_rows(case: dict, causal: bool, sel: np.ndarray):
-    """The oracle on rows sel; K and V may have their own [B, Hkv, Nk, d] shape."""
+def run_masked(case: dict, causal: bool, mask: np.ndarray, n_splits=None, inputs=None,
+               mask_dev=None):
+    """attn_fwd_masked (n_splits None) or attn_fwd_masked_splitkv with an fp32
+    mask of shape [Nq, Nk] or [B|1, H|1, Nq, Nk]."""
+    import exact_self_attention_amd as attn
+    q, k, v, kl = inputs if inputs is not None else dev_inputs(case)
+    m = mask_dev if mask_dev is not None else torch.from_numpy(np.ascontiguousarray(mask)).to(device())
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if n_splits is None:
+        attn.attn_fwd_masked(q, k, v, o, lse, mask=m, scale=float(case["scale"]), causal=causal,
+                             key_len=kl)
+    else:
+        B, H, Nq, d = q.shape
+        nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+        attn.attn_fwd_masked_splitkv(q, k, v, o, lse, mask=m, workspace=ws, n_splits=n_splits,
+                                     scale=float(case["scale"]), causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return from_dev(o, case["dtype"]), lse.cpu().numpy()
+
+
+def oracle_rows(case: dict, causal: bool, sel: np.ndarray, mask=None):
+    """The oracle on rows sel; K and V may have their own [B, Hkv, Nk, d]
+    shape; ``mask`` an additive fp32 mask ([Nq, Nk] or [B|1, H|1, Nq, Nk])."""
     dt = case["dtype"]
     Q = ai.bits_to_f32(case["Q"], dt)
     K = ai.bits_to_f32(case["K"], dt)
     V = ai.bits_to_f32(case["V"], dt)
-    return oracle.attn_rows(Q, K, V, float(case["scale"]), causal, case.get("key_len"), sel)
+    return oracle.attn_rows(Q, K, V, float(case["scale"]), causal, case.get("key_len"), sel,
+                            mask=mask)
 
 
 def sample_rows(B: int, H: int, N: int, per_head: int, seed: int) -> np.ndarray:

@@ -227,3 +227,27 @@ def test_gqa_split_and_default_splits_without_device(lib):
     assert lib.lib.attn_fwd_gqa_splitkv(*a, 0, A + 256 * MB, need, None) == INVALID
     assert lib.attn_fwd_gqa_splitkv_default_splits(0, 1, 8, 3, 1, 4096, 128, True) == 1
     assert lib.attn_fwd_gqa_splitkv_default_splits(0, 1, 8, 2, 1, 4096, 128, True) >= 1
+
+
+def call_masked(lib, mask=A + 320 * MB, sb=0, sh=0, **kw):
+    a = dict(dtype=0, Q=A, K=A + 64 * MB, V=A + 128 * MB, O=A + 192 * MB, LSE=None,
+             B=2, H=8, Hkv=2, Nq=64, Nk=128, d=64, scale=0.125, causal=0, key_len=None)
+    a.update(kw)
+    return lib.lib.attn_fwd_masked(a["dtype"], a["Q"], a["K"], a["V"], a["O"], a["LSE"],
+                                   a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                   a["scale"], a["causal"], a["key_len"], mask, sb, sh, None)
+
+
+def test_masked_argument_checks(lib):
+    assert call_masked(lib, mask=None) == INVALID
+    assert call_masked(lib, sb=-1) == INVALID
+    assert call_masked(lib, sh=-64) == INVALID
+    assert call_masked(lib, mask=A + 320 * MB + 2) == MISALIGNED
+    assert call_masked(lib, sh=1 << 27) == INVALID              # one batch's mask >= 2 GiB
+    assert call_masked(lib, mask=A + 192 * MB + 64) == INVALID  # mask overlaps O
+    assert call_masked(lib, Hkv=3) == INVALID
+    assert call_masked(lib, B=0) == 0                            # empty: no-op
+    assert call_masked(lib, mask=None, B=0) == INVALID
+    # the mask may share memory with the read-only inputs; stops at the device check here
+    assert call_masked(lib, mask=A + 64 * MB, sb=64 * 128, sh=0) in (0, DEVICE)
+    assert call_masked(lib, sb=8 * 64 * 128, sh=64 * 128) in (0, DEVICE)

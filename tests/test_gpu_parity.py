@@ -376,3 +376,78 @@ def test_gqa_workload_matches_oracle(cases, name):
     gu.log(f"{name}: default splits {S}")
     Og, Lg = gu.gather(O, LSE, sel)
     gu.assert_close(Og, Lg, O_ref, LSE_ref, w.dtype, f"{name} split S={S}", sel)
+
+
+# Additive fp32 mask (attn_fwd_masked): shared [Nq, Nk] masks, per-head and
+# per-batch masks, masks with -inf elements and rows that are -inf
+# throughout, with and without the causal and key-length masks, every d and
+# both dtypes, grouped heads and Nq != Nk, short key lengths (which take the
+# streaming kernel when masked).  Every row is checked.
+MASK_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, causal, dtype, key_len, mask shape kind, -inf fraction)
+    (1, 4, 4, 700, 700, 128, True, ai.F16, None, "shared", 0.0),
+    (2, 4, 2, 300, 1000, 128, False, ai.BF16, [1000, 421], "per_head", 0.0),
+    (2, 6, 3, 257, 257, 64, True, ai.F16, None, "per_batch", 0.3),
+    (2, 8, 8, 100, 600, 64, True, ai.BF16, [600, 1], "shared", 0.1),
+    (3, 4, 1, 77, 200, 32, False, ai.F16, [200, 0, 150], "per_head", 0.2),
+    (1, 4, 2, 513, 130, 32, True, ai.BF16, None, "shared", 0.0),
+    (2, 2, 2, 64, 64, 128, False, ai.F16, None, "per_batch", 0.5),
+]
+
+
+def _mask_shape(kind, B, H, Nq, Nk):
+    return {"shared": (Nq, Nk), "per_head": (B, H, Nq, Nk), "per_batch": (B, 1, Nq, Nk)}[kind]
+
+
+def _mask_id(c):
+    B, H, Hkv, Nq, Nk, d, causal, dtype, kl, kind, frac = c
+    return (f"B{B}H{H}kv{Hkv}q{Nq}k{Nk}d{d}{'c' if causal else 'f'}{dtype}"
+            f"{'' if kl is None else 'L'}-{kind}-inf{frac}")
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal,dtype,kl,kind,frac", MASK_CASES,
+                         ids=[_mask_id(c) for c in MASK_CASES])
+def test_masked_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, kind, frac):
+    case = _gqa_case(B, H, Hkv, Nq, Nk, d, causal, dtype, kl, 60_000)
+    mask = ai.random_mask(_mask_shape(kind, B, H, Nq, Nk), seed=case["seed"] + 1, sigma=2.0,
+                          neg_inf_frac=frac, empty_rows=(min(5, Nq - 1),) if frac > 0 else ())
+    gu.log(f"masked {_mask_id((B, H, Hkv, Nq, Nk, d, causal, dtype, kl, kind, frac))}")
+    sel = ai.all_rows_selection(B, H, Nq)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel, mask=mask)
+    O, LSE = gu.run_masked(case, causal, mask)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"masked {kind}", sel)
+    O, LSE = gu.run_masked(case, causal, mask, n_splits=3)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"masked split {kind}", sel)
+
+
+def test_zero_mask_equals_unmasked_and_expand_views():
+    # an all-zero mask gives attn_fwd_gqa's result (same tiles, same order:
+    # the mask adds exactly 0); a [Nq, Nk] mask expanded to [B, H, Nq, Nk]
+    # (stride-0 view) equals the same mask copied out
+    B, H, Hkv, Nq, Nk, d = 2, 4, 2, 300, 500, 64
+    case = ai.random_case_general(B, H, Hkv, Nq, Nk, d, ai.BF16, seed=61_000, key_len=[500, 77])
+    inputs = gu.dev_inputs(case)
+    zero = np.zeros((Nq, Nk), np.float32)
+    O0, L0 = gu.run_masked(case, True, zero, inputs=inputs)
+    O1, L1 = gu.run_gqa(case, True, inputs=inputs)
+    sel = ai.all_rows_selection(B, H, Nq)
+    gu.assert_close(*gu.gather(O0, L0, sel), *[np.asarray(x, np.float64) for x in gu.gather(O1, L1, sel)],
+                    ai.BF16, "zero mask vs unmasked", sel)
+    m = ai.random_mask((Nq, Nk), seed=61_001)
+    md = torch.from_numpy(m).to(gu.device())
+    O2, L2 = gu.run_masked(case, True, m, inputs=inputs, mask_dev=md.expand(B, H, Nq, Nk))
+    O3, L3 = gu.run_masked(case, True, m, inputs=inputs,
+                           mask_dev=md.expand(B, H, Nq, Nk).contiguous())
+    assert np.array_equal(O2, O3) and np.array_equal(L2, L3)
+
+
+def test_masked_prefill_workload():
+    w = ai.WORKLOADS["masked_prefill"]
+    case = ai.generate(w)
+    sel = gu.sample_rows(w.B, w.H, w.q_len, 32, seed=w.seed + 7)
+    O_ref, LSE_ref = gu.oracle_rows(case, w.causal, sel, mask=case["mask"])
+    gu.log("masked_prefill: fused")
+    O, LSE = gu.run_masked(case, w.causal, case["mask"])
+    gu.assert_close(*gu.gather(O, LSE, sel), O_ref, LSE_ref, w.dtype, "masked_prefill", sel)
