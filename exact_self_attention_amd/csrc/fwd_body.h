@@ -494,10 +494,17 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
             }
         }
         if (!kSpreadLoads && (ph & 1) == 0 && is_loader) issue_batch(ph >> 1, k_next, v_next);
-        // the newest batch (and with a mask the 8 mask loads issued after
-        // it) may stay in flight
-        if (ph & 1) wait_tile_loads<(kAhead - 1) * SHARE + (MASK ? 8 : 0)>();
-        barrier();
+        // Tiles are published and ring slots released only at the end of
+        // odd phases (the newest batch, and with a mask the 8 mask loads
+        // issued after it, may stay in flight), so that is the only place a
+        // workgroup barrier is needed.  Between two of them each wave runs
+        // its matrix-core phase and its softmax phase back to back: the two
+        // waves of a SIMD start them in opposite order, so they still
+        // overlap, and the waves are not forced into step twice per tile.
+        if (ph & 1) {
+            wait_tile_loads<(kAhead - 1) * SHARE + (MASK ? 8 : 0)>();
+            barrier();
+        }
     };
 
     // prologue: K tile 0, then the batches of the virtual phases -2(kAhead-1)
