@@ -336,12 +336,8 @@ def main():
     key_len = case["key_len"]
     pairs = visible_pairs(w, key_len)
     F_alg = 4.0 * w.d * pairs
-    kernel = attn.attn_fwd_kernel_name(code, w.d, w.N, w.causal, key_len is not None)
-    tail = f"d{w.d}_{w.dtype}_{'causal' if w.causal else 'full'}"
-    if n_splits is not None:  # the split form always runs the streaming kernel
-        kernel = f"attn_fwd_split_{'mask_' if mask is not None else ''}{tail}"
-    elif mask is not None:  # and so does the masked form
-        kernel = f"attn_fwd_mask_{tail}"
+    kernel = attn.attn_fwd_gqa_kernel_name(code, w.d, w.H, w.kv_heads, w.q_len, w.N, w.causal,
+                                           mask is not None, n_splits or 0)
     nbytes = algorithmic_bytes(w, key_len)
     # the bound: HBM when the flops per algorithmic byte are below the
     # machine balance (matrix-core peak / HBM bandwidth), else the matrix cores

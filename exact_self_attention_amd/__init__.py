@@ -28,7 +28,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
 EXPORTS = ["attn_fwd", "attn_fwd_gqa", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_gqa_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_splitkv_default_splits", "attn_fwd_gqa_splitkv_default_splits",
-           "attn_fwd_masked", "attn_fwd_masked_splitkv",
+           "attn_fwd_masked", "attn_fwd_masked_splitkv", "attn_fwd_gqa_kernel_name",
            "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
 
 
@@ -72,6 +72,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_fwd_kernel_name.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, ctypes.c_size_t]
     lib.attn_fwd_kernel_name.restype = i32
+    lib.attn_fwd_gqa_kernel_name.argtypes = [i32, i64, i64, i64, i64, i64, i32, i32, i64,
+                                             ctypes.c_char_p, ctypes.c_size_t]
+    lib.attn_fwd_gqa_kernel_name.restype = i32
     lib.attn_version.argtypes = []
     lib.attn_version.restype = i32
     return lib
@@ -290,6 +293,16 @@ def attn_fwd_kernel_name(dtype: int, d: int, N: int, causal: bool, has_key_len: 
     st = lib.attn_fwd_kernel_name(dtype, d, N, int(bool(causal)), int(bool(has_key_len)), buf, 128)
     if st != 0:
         raise AttnError("attn_fwd_kernel_name", st)
+    return buf.value.decode()
+
+
+def attn_fwd_gqa_kernel_name(dtype: int, d: int, H: int, Hkv: int, Nq: int, Nk: int,
+                             causal: bool, masked: bool = False, n_splits: int = 0) -> str:
+    buf = ctypes.create_string_buffer(128)
+    st = lib.attn_fwd_gqa_kernel_name(dtype, d, H, Hkv, Nq, Nk, int(bool(causal)), int(bool(masked)),
+                                      int(n_splits), buf, 128)
+    if st != 0:
+        raise AttnError("attn_fwd_gqa_kernel_name", st)
     return buf.value.decode()
 
 

@@ -356,10 +356,17 @@ int64_t attn_fwd_gqa_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64
         Nq > kMaxN || Nk > kMaxN || H > INT32_MAX / B || (H / Hkv) * Nq > kMaxN)
         return 1;
     if (check_device() != ATTN_OK) return 1;
-    const int resident = attn::fwd_split_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0);
+    attn::FwdParams probe = make_params(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                        Shape{B, H, Hkv, Nq, Nk, d}, 1.f, nullptr);
+    const bool decode = attn::fwd_uses_decode(probe);
+    const int resident =
+        decode ? attn::fwd_decode_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0)
+               : attn::fwd_split_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0);
     if (resident <= 0) return 1;
+    // work items: (key/value head, 256-row query tile), or one per key/value
+    // head for the decode kernel
     const int64_t rows = attn::fwd_query_rows_per_item();
-    const int64_t items = ((H / Hkv) * Nq + rows - 1) / rows * B * Hkv;
+    const int64_t items = decode ? B * Hkv : ((H / Hkv) * Nq + rows - 1) / rows * B * Hkv;
     if (items >= resident) return 1;
     const int64_t tiles = (Nk + 63) / 64;
     int64_t s = (resident + items - 1) / items;
@@ -403,6 +410,37 @@ attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N, int
     if (N < 0 || N > kMaxN) return ATTN_ERR_INVALID_ARG;
     if (buf == nullptr || buf_len == 0) return ATTN_ERR_INVALID_ARG;
     std::snprintf(buf, buf_len, "%s", attn::fwd_kernel_name(dtype == ATTN_BF16, (int)d, causal != 0, N));
+    return ATTN_OK;
+}
+
+attn_status_t attn_fwd_gqa_kernel_name(attn_dtype_t dtype, int64_t d, int64_t H, int64_t Hkv,
+                                       int64_t Nq, int64_t Nk, int causal, int masked,
+                                       int64_t n_splits, char *buf, size_t buf_len) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (H < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0 || Nq < 0 || Nk < 0 || Nq > kMaxN ||
+        Nk > kMaxN || (H / Hkv) * Nq > kMaxN || n_splits < 0 || n_splits > kMaxSplits)
+        return ATTN_ERR_INVALID_ARG;
+    if (buf == nullptr || buf_len == 0) return ATTN_ERR_INVALID_ARG;
+    const bool bf16 = dtype == ATTN_BF16;
+    const bool split = n_splits > 0;
+    attn::FwdParams p = make_params(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    Shape{1, H, Hkv, Nq, Nk, d}, 1.f, nullptr);
+    p.mask = masked ? reinterpret_cast<const float *>(&p) : nullptr;  // only its presence matters
+    const char *name;
+    if (masked)
+        name = attn::fwd_masked_kernel_name(bf16, (int)d, causal != 0, split);
+    else if (!split && Nk <= attn::fwd_short_max_keys((int)d))
+        name = attn::fwd_kernel_name(bf16, (int)d, causal != 0, Nk);
+    else if (attn::fwd_uses_decode(p))
+        name = attn::fwd_decode_kernel_name(bf16, (int)d, causal != 0, split);
+    else if (attn::fwd_uses_deep(p))
+        name = attn::fwd_deep_kernel_name(bf16, (int)d, causal != 0, split);
+    else if (split)
+        name = attn::fwd_split_kernel_name(bf16, (int)d, causal != 0);
+    else
+        name = attn::fwd_fused_kernel_name(bf16, (int)d, causal != 0);
+    std::snprintf(buf, buf_len, "%s", name);
     return ATTN_OK;
 }
 

@@ -128,8 +128,28 @@ __device__ __forceinline__ void sched_steps() {
 // than the mask.  With a mask every wave issues tile loads at the start of
 // its softmax phase, and at d = 128 Q fragments are read from LDS instead of
 // being held in VGPRs (the mask values take those registers).
-template <int D, bool BF16, bool CAUSAL, bool SPLIT, bool MASK>
+// LDS for the query tile, allocated only by the instances that stage it.
+template <int HALVES>
+struct QStage {
+    __device__ static uint16_t *get() {
+        __shared__ __attribute__((aligned(1024))) uint16_t buf[HALVES];
+        return buf;
+    }
+};
+template <>
+struct QStage<0> {
+    __device__ static uint16_t *get() { return nullptr; }
+};
+
+// DEEP: for slices of at most one query tile (decode-like shapes, which
+// stream K/V and are bound by device memory), Q goes from device memory
+// straight to registers instead of through LDS, and the freed LDS deepens
+// the K/V rings to 5 slots, so 4 tiles of loads are in flight instead of 2.
+template <int D, bool BF16, bool CAUSAL, bool SPLIT, bool MASK, bool DEEP = false>
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
+    static_assert(!(DEEP && MASK), "the deep-ring instances have no mask");
+    constexpr int RING = DEEP ? 5 : kRing;
+    constexpr int AHEAD = RING - 1;
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int TILE = kBN * D;                 // halves per K or V tile
     constexpr int TILE_INSTR = kBN * CPR / 64;    // 1 KB load instructions per tile
@@ -137,9 +157,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     constexpr int DK = D / 16;                    // 16-deep k-steps of Q.K
     constexpr int DB = D / 32;                    // 32-wide column blocks of O
 
-    __shared__ __attribute__((aligned(1024))) uint16_t sQ[kBM * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[kRing][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[kRing][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[RING][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[RING][TILE];
+    uint16_t *const sQ = QStage<DEEP ? 0 : kBM * D>::get();
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -203,7 +223,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // The query tile goes to LDS once (same swizzled row-major layout as the
     // K tiles; rows past N read as zero); each wave re-reads its Q fragments
     // there instead of holding them in 8 x DK VGPRs.
-    {
+    if constexpr (!DEEP) {
         constexpr int QI = kBM * CPR / 64;        // 1 KB load instructions
         static_assert(QI % kWaves == 0, "query tile load split");
         const int rows = min(kBM, M - q0);
@@ -223,7 +243,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // fills LDS bytes [1024 t, 1024 t + 1024); lane i writes 16 bytes at
     // 1024 t + 16 i, i.e. physical chunk P = 64 t + i = row * CPR + chunk'.
     // The lane therefore fetches logical chunk chunk' ^ swz(row).
-    // Batch jb is K tile jb + kAhead and V tile jb + kAhead - 1 (2 TILE_INSTR
+    // Batch jb is K tile jb + AHEAD and V tile jb + AHEAD - 1 (2 TILE_INSTR
     // instructions); each of the NLD loader waves issues SHARE of them,
     // instruction t = wave + NLD i (K for t < TILE_INSTR, then V).  Issuing a
     // 1 KB load can stall the issuing wave while the vector memory front end
@@ -258,8 +278,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         return make_rsrc(src + (size_t)(j < n ? j0 : 0) * D, (uint32_t)(rows * D * 2));
     };
     auto issue_batch = [&](int jb, const uint16_t *k_dst, const uint16_t *v_dst) {
-        const i32x4 rk = tile_rsrc(Kp, jb + kAhead);
-        const i32x4 rv = tile_rsrc(Vp, jb + kAhead - 1);
+        const i32x4 rk = tile_rsrc(Kp, jb + AHEAD);
+        const i32x4 rv = tile_rsrc(Vp, jb + AHEAD - 1);
         const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)k_dst;
         const uint32_t vl = (uint32_t)(uintptr_t)(lds_void *)v_dst;
 #pragma unroll
@@ -457,12 +477,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // One phase.  Group A (grp 0) issues the MFMA work of pair j in phase 2j
     // and the softmax of tile j in phase 2j+1; group B runs one phase later.
     // K tile j is read in phases 2j and 2j+1, V tile j in 2j+2 and 2j+3.
-    // Batch j (K tile j+kAhead, V tile j+kAhead-1, both first read in phase
-    // 2(j+kAhead)) is issued in phase 2j (group A, after its matrix-core
+    // Batch j (K tile j+AHEAD, V tile j+AHEAD-1, both first read in phase
+    // 2(j+AHEAD)) is issued in phase 2j (group A, after its matrix-core
     // work) or, with kSpreadLoads, by group B in phase 2j and group A in
     // phase 2j+1 (at the start of their softmax of tile j).  It is waited for
-    // at the end of phase 2(j+kAhead)-1, when each loader's share of the
-    // kAhead-1 later batches may still be in flight.  Its slots were last
+    // at the end of phase 2(j+AHEAD)-1, when each loader's share of the
+    // AHEAD-1 later batches may still be in flight.  Its slots were last
     // read in phase 2j-1.  Slot arrays are passed in statically so the
     // compiler can tell the in-flight loads from the tiles being read.
     auto phase = [&](int ph, const uint16_t *k_cur, const uint16_t *v_prev,
@@ -502,13 +522,25 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         // waves of a SIMD start them in opposite order, so they still
         // overlap, and the waves are not forced into step twice per tile.
         if (ph & 1) {
-            wait_tile_loads<(kAhead - 1) * SHARE + (MASK ? 8 : 0)>();
+            wait_tile_loads<(AHEAD - 1) * SHARE + (MASK ? 8 : 0)>();
             barrier();
         }
     };
 
-    // prologue: K tile 0, then the batches of the virtual phases -2(kAhead-1)
-    // .. -2 (K tiles 1 .. kAhead-1 and V tiles 0 .. kAhead-2); only K tile 0
+    if constexpr (DEEP) {
+        // this wave's Q fragments straight from device memory (rows past M
+        // are zero), waited for here, before any tile load is issued (the
+        // compiler's wait for them then covers no tile load)
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk)
+            qreg[kk] = my_q < M ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + (2 * kk + g) * 8)
+                                : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) asm volatile("" ::"v"(qreg[kk]));
+    }
+
+    // prologue: K tile 0, then the batches of the virtual phases -2(AHEAD-1)
+    // .. -2 (K tiles 1 .. AHEAD-1 and V tiles 0 .. AHEAD-2); only K tile 0
     // (and the Q tile) must have arrived before the first phase.
     const int n_phases = n > 0 ? 2 * n + 2 : 0;
     if (n > 0 && is_loader) {
@@ -518,9 +550,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         for (int i = 0; i < SHARE; ++i)
             if (!ld_is_v[i]) dma16(rk, kl + lds_off[i], voff[i]);
 #pragma unroll
-        for (int jb = 1 - kAhead; jb < 0; ++jb)
-            issue_batch(jb, sK[(jb + kAhead) % kRing], sV[(jb + kAhead - 1) % kRing]);
-        wait_tile_loads<(kAhead - 1) * SHARE>();
+        for (int jb = 1 - AHEAD; jb < 0; ++jb)
+            issue_batch(jb, sK[(jb + AHEAD) % RING], sV[(jb + AHEAD - 1) % RING]);
+        wait_tile_loads<(AHEAD - 1) * SHARE>();
     } else {
         wait_tile_loads<0>();
     }
@@ -529,20 +561,20 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // loads a mask (group B loads tile 0's in its first phase)
     if (MASK && grp == 0) issue_mask(0);
 
-    if constexpr (kQInRegs) {
+    if constexpr (kQInRegs && !DEEP) {
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) qreg[kk] = frag_q(kk);
     }
 
-    // Phases 2 kRing i + 2u and + 1 handle tile j = kRing i + u, whose K tile
+    // Phases 2 RING i + 2u and + 1 handle tile j = RING i + u, whose K tile
     // sits in slot u; slots therefore depend only on the unrolled position.
-    for (int ph = 0; ph < n_phases; ph += 2 * kRing) {
+    for (int ph = 0; ph < n_phases; ph += 2 * RING) {
 #pragma unroll
-        for (int u = 0; u < 2 * kRing; ++u) {
+        for (int u = 0; u < 2 * RING; ++u) {
             const int t = u >> 1;
             if (ph + u < n_phases)
-                phase(ph + u, sK[t], sV[(t + kRing - 1) % kRing], sK[(t + kAhead) % kRing],
-                      sV[(t + kAhead - 1) % kRing]);
+                phase(ph + u, sK[t], sV[(t + RING - 1) % RING], sK[(t + AHEAD) % RING],
+                      sV[(t + AHEAD - 1) % RING]);
         }
     }
     // loads of tiles past the last one (empty ranges) may still be in flight

@@ -139,13 +139,17 @@ const char *fwd_fused_kernel_name(bool bf16, int d, bool causal) {
     return entry(bf16, d, causal).name;
 }
 
+bool fwd_uses_deep(const FwdParams &p) { return p.mask == nullptr && p.M <= kBM; }
+
 hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
+    if (fwd_uses_decode(p)) return launch_fwd_decode(bf16, d, causal, false, p, s);
     p.n_qtiles = (int)((p.M + kBM - 1) / kBM);
     const int64_t blocks = (int64_t)p.n_qtiles * p.slices;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const FwdKernelFn fn = p.mask != nullptr ? fwd_masked_kernel(bf16, d, causal, false)
-                                             : entry(bf16, d, causal).fn;
+                           : fwd_uses_deep(p) ? fwd_deep_kernel(bf16, d, causal, false)
+                                              : entry(bf16, d, causal).fn;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
@@ -182,10 +186,16 @@ hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStrea
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL || p.kv_splits < 1 || p.split_tiles < 1)
         return hipErrorInvalidConfiguration;
-    const FwdKernelFn fn = p.mask != nullptr ? fwd_masked_kernel(bf16, d, causal, true)
-                                             : kSplitTable[table_index(bf16, d, causal)].fn;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (fwd_uses_decode(p)) {
+        e = launch_fwd_decode(bf16, d, causal, true, p, s);
+    } else {
+        const FwdKernelFn fn = p.mask != nullptr ? fwd_masked_kernel(bf16, d, causal, true)
+                               : fwd_uses_deep(p) ? fwd_deep_kernel(bf16, d, causal, true)
+                                                  : kSplitTable[table_index(bf16, d, causal)].fn;
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     MergeParams m;
     m.part_O = p.part_O;

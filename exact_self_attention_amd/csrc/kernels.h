@@ -69,6 +69,21 @@ int fwd_query_rows_per_item();
 FwdKernelFn fwd_masked_kernel(bool bf16, int d, bool causal, bool split);
 const char *fwd_masked_kernel_name(bool bf16, int d, bool causal, bool split);
 
+// Streaming kernel instances with 5-slot rings and Q straight to registers
+// (fwd_deep.hip) for slices of at most one 256-row query tile without a
+// mask; launch_fwd_fused and launch_fwd_split take them then.
+FwdKernelFn fwd_deep_kernel(bool bf16, int d, bool causal, bool split);
+const char *fwd_deep_kernel_name(bool bf16, int d, bool causal, bool split);
+bool fwd_uses_deep(const FwdParams &p);
+
+// Decode kernel (fwd_decode.hip) for slices of at most 32 query rows
+// without a mask: 4 waves split the key range and merge at the end;
+// launch_fwd_fused and launch_fwd_split take it then.
+bool fwd_uses_decode(const FwdParams &p);
+hipError_t launch_fwd_decode(bool bf16, int d, bool causal, bool split, FwdParams p, hipStream_t s);
+const char *fwd_decode_kernel_name(bool bf16, int d, bool causal, bool split);
+int fwd_decode_resident_workgroups(bool bf16, int d, bool causal);
+
 // Short-sequence kernel (Nk <= fwd_short_max_keys(d)): 4 waves, 128 query
 // rows per workgroup, the slice's whole K and V resident in LDS.
 int64_t fwd_short_max_keys(int d);

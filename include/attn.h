@@ -282,6 +282,19 @@ attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N,
                                    int causal, int has_key_len,
                                    char *buf, size_t buf_len);
 
+/*
+ * Name of the kernel instance the general entry points launch for these
+ * arguments (for profilers): attn_fwd_gqa (masked = 0, n_splits = 0),
+ * attn_fwd_gqa_splitkv (n_splits > 0) or the masked forms (masked != 0);
+ * with splits the merge kernel runs after it.  Written into buf
+ * (NUL-terminated, truncated to buf_len).  Returns ATTN_ERR_UNSUPPORTED or
+ * ATTN_ERR_INVALID_ARG for arguments those entry points reject, else
+ * ATTN_OK.  Touches no device state.
+ */
+attn_status_t attn_fwd_gqa_kernel_name(attn_dtype_t dtype, int64_t d, int64_t H, int64_t Hkv,
+                                       int64_t Nq, int64_t Nk, int causal, int masked,
+                                       int64_t n_splits, char *buf, size_t buf_len);
+
 /* Library ABI version (major * 100 + minor). */
 int attn_version(void);
 

@@ -251,3 +251,27 @@ def test_masked_argument_checks(lib):
     # the mask may share memory with the read-only inputs; stops at the device check here
     assert call_masked(lib, mask=A + 64 * MB, sb=64 * 128, sh=0) in (0, DEVICE)
     assert call_masked(lib, sb=8 * 64 * 128, sh=64 * 128) in (0, DEVICE)
+
+
+def test_gqa_kernel_names(lib):
+    f16, bf16 = 0, 1
+    assert lib.attn_fwd_gqa_kernel_name(f16, 128, 32, 32, 4096, 4096, True) == "attn_fwd_d128_f16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 32, 12, 12, 256, 256, False) == "attn_fwd_short_d32_f16_full"
+    # at most 32 query rows per key/value head: the decode kernel
+    assert lib.attn_fwd_gqa_kernel_name(bf16, 128, 32, 8, 1, 32768, True) == "attn_fwd_decode_d128_bf16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(bf16, 128, 32, 8, 1, 32768, True, n_splits=4) == \
+        "attn_fwd_split_decode_d128_bf16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 64, 32, 8, 8, 1000, False) == "attn_fwd_decode_d64_f16_full"
+    # at most one 256-row query tile per key/value head: the deep-ring instances
+    assert lib.attn_fwd_gqa_kernel_name(bf16, 128, 32, 8, 16, 32768, True) == "attn_fwd_deep_d128_bf16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(bf16, 128, 32, 8, 64, 32768, True, n_splits=4) == \
+        "attn_fwd_split_deep_d128_bf16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 64, 32, 8, 65, 4096, False) == "attn_fwd_d64_f16_full"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 128, 4, 4, 4096, 4096, True, n_splits=4) == \
+        "attn_fwd_split_d128_f16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 128, 32, 32, 4096, 4096, True, masked=True) == \
+        "attn_fwd_mask_d128_f16_causal"
+    assert lib.attn_fwd_gqa_kernel_name(f16, 128, 32, 8, 1, 4096, True, masked=True, n_splits=2) == \
+        "attn_fwd_split_mask_d128_f16_causal"
+    with pytest.raises(lib.AttnError):
+        lib.attn_fwd_gqa_kernel_name(f16, 128, 32, 3, 1, 4096, True)

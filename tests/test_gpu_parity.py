@@ -294,6 +294,10 @@ GQA_CASES = [
     (1, 4, 4, 33, 250, 64, False, ai.F16, None),
     (2, 6, 2, 300, 64, 64, True, ai.F16, [64, 0]),
     (1, 8, 2, 64, 0, 64, True, ai.F16, None),
+    # at most 32 query rows per key/value head (the decode kernel)
+    (2, 8, 2, 8, 1500, 64, True, ai.BF16, [1500, 333]),
+    (1, 4, 1, 7, 300, 32, True, ai.F16, None),
+    (2, 4, 4, 3, 129, 128, True, ai.F16, [129, 64]),
 ]
 
 
@@ -327,6 +331,8 @@ GQA_SPLIT_CASES = [
     (1, 6, 1, 700, 300, 128, True, ai.F16, None, 4),
     (2, 12, 3, 20, 700, 32, True, ai.BF16, [700, 650], 5),
     (2, 8, 8, 1, 600, 64, False, ai.F16, [600, 0], 64),
+    (2, 8, 2, 8, 1500, 64, True, ai.BF16, [1500, 333], 5),
+    (1, 4, 1, 7, 300, 32, True, ai.F16, None, 2),
 ]
 
 
