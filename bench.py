@@ -35,8 +35,8 @@ METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal ×½) + % of MI355X MFMA pea
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_self_attention_amd", "csrc", f)
-                  for f in ("cdna4.h", "dispatch.cpp", "fwd_body.h", "fwd_fused.hip", "fwd_masked.hip",
-                            "fwd_short.hip")]
+                  for f in ("cdna4.h", "dispatch.cpp", "fwd_body.h", "fwd_decode.hip", "fwd_deep.hip",
+                            "fwd_fused.hip", "fwd_masked.hip", "fwd_short.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 COPY_PROBE_BYTES = 1 << 30
 
