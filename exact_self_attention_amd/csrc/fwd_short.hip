@@ -1,28 +1,31 @@
 // Fused exact attention forward for short sequences on gfx950 (CDNA4).
 //
-// When a slice's keys fit in LDS (Nk <= 256 at d <= 64, Nk <= 128 at
-// d = 128) the streaming pipeline of the long-sequence kernel only adds
-// latency: every tile is used once and the loop is a few tiles long.  Here a
-// workgroup of 4 waves owns 128 query rows of one slice (b, key/value head;
-// the rows of the query heads that share it, head after head):
+// For short key ranges (Nk <= 256 at d <= 64, Nk <= 128 at d = 128) the
+// streaming kernel's deep pipeline and wave specialisation only add latency:
+// a slice has at most four 64-key tiles.  Here a workgroup of 4 waves owns
+// 128 query rows of one slice (b, key/value head; the rows of the query
+// heads that share it, head after head):
 //
-//   1. all of the slice's visible K and V rows go to LDS at once (direct
-//      buffer loads, rows past the valid key length read as zero and are not
-//      fetched), and each wave loads the Q fragments of its query rows
-//      straight into VGPRs;
-//   2. one barrier;
-//   3. each wave runs, for every key tile its 32 rows can see,
+//   1. each wave loads the Q fragments of its query rows straight into
+//      VGPRs, and the workgroup loads the first key tiles (K and V) into an
+//      LDS ring (as many slots as short_ring_of(d)) with direct buffer loads
+//      (rows past the valid key length read as zero and are not fetched);
+//   2. for every key tile its 32 rows can see, each wave runs
 //      S^T = K_j Q^T on the matrix cores, the online softmax update of
 //      "Self-Attention Kernel & Inference Engine from Scratch" (section
 //      "Online Softmax Formulation": running max, running normaliser,
-//      rescaled output), and O^T += V_j^T P^T, with no further
-//      synchronisation, then writes O = O_acc / l and LSE.
+//      rescaled output), and O^T += V_j^T P^T.  When a slice has more
+//      tiles than slots, one barrier per tile frees the slot of the
+//      previous tile, and the tile RING - 1 ahead is loaded into it;
+//   3. O = O_acc / l goes through LDS to coalesced stores, with LSE.
 //
-// A workgroup needs at most 64 KB of LDS (32 KB at d = 32), so several are
-// resident per compute unit and their load latencies overlap each other's
-// arithmetic.  Masking follows the long-sequence kernel: causal and key-length
-// limits end the tile loop early and per-element masks run only on tiles
-// that straddle a limit; a masked score is -inf, whose exp2 is exactly 0.
+// A workgroup needs 32 KB of LDS at d = 32, 48 KB at d = 64 and 64 KB at
+// d = 128, and 4, 3 or 2 workgroups are resident per compute unit.  (Five
+// of 32 KB do not fit on gfx950, although the occupancy query reports 5; at
+// 31 KB five do.)  Masking follows the long-sequence kernel: causal and
+// key-length limits end the tile loop early and per-element masks run only
+// on tiles that straddle a limit; a masked score is -inf, whose exp2 is
+// exactly 0.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,16 +44,24 @@ constexpr int short_max_keys_of(int d) { return d >= 128 ? 128 : 256; }
 // workgroup making two passes, measured slower: fewer waves in flight.)
 constexpr int kSWaves = 4;
 constexpr int kSBM = kSWaves * kQRows;
+// LDS slots for K and V tiles: all four tiles at d = 32 (32 KB), a ring of
+// three at d = 64 (48 KB instead of 64: 3 workgroups per compute unit
+// instead of 2, measured 18% faster at 256 keys), both tiles at d = 128
+// (64 KB).  At d = 32 a ring of 2 or 3 (5 workgroups per compute unit)
+// measured no faster: the softmax arithmetic, not the latency, bounds it.
+constexpr int short_ring_of(int d) { return d == 64 ? 3 : short_max_keys_of(d) / kBN; }
 // Waves per SIMD the register allocation must allow: as many workgroups as
-// LDS holds per compute unit (4 of 32 KB at d = 32, 2 of 64 KB otherwise).
-constexpr int short_waves_per_simd(int d) { return d == 32 ? 4 : 2; }
+// LDS holds per compute unit.
+constexpr int short_waves_per_simd(int d) { return d == 32 ? 4 : (d == 64 ? 3 : 2); }
 
 template <int D, bool BF16, bool CAUSAL>
 __device__ __forceinline__ void short_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int TILE = kBN * D;                 // halves per K or V tile
     constexpr int TILE_INSTR = kBN * CPR / 64;    // 1 KB load instructions per tile
-    constexpr int NT = short_max_keys_of(D) / kBN;  // key tiles held in LDS
+    constexpr int NT = short_max_keys_of(D) / kBN;  // key tiles of a slice at most
+    constexpr int RING = short_ring_of(D);        // LDS slots per K and V
+    static_assert(RING >= 2 && RING <= NT, "ring depth");
     constexpr int SW = kSWaves;
     constexpr int SHARE = 2 * TILE_INSTR / SW;    // K and V loads per wave per tile
     constexpr int KB = kBN / 32;
@@ -59,8 +70,8 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     static_assert((2 * TILE_INSTR) % SW == 0, "tile load split");
     static_assert(KB == 2, "the softmax arithmetic assumes 64-key tiles");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[NT][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[NT][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[RING][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[RING][TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -119,14 +130,13 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     for (int kk = 0; kk < DK; ++kk)
         qreg[kk] = my_q < M ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + (2 * kk + g) * 8)
                             : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    auto issue_tile = [&](int t) {
         if (t < n) {
             const int rows = min(kBN, Lk - t * kBN);
             const i32x4 rk = make_rsrc(Kp + (size_t)t * kBN * D, (uint32_t)(rows * D * 2));
             const i32x4 rv = make_rsrc(Vp + (size_t)t * kBN * D, (uint32_t)(rows * D * 2));
-            const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)sK[t];
-            const uint32_t vl = (uint32_t)(uintptr_t)(lds_void *)sV[t];
+            const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)sK[t % RING];
+            const uint32_t vl = (uint32_t)(uintptr_t)(lds_void *)sV[t % RING];
 #pragma unroll
             for (int i = 0; i < SHARE; ++i) {
                 const int u = wave_u + SW * i;
@@ -142,8 +152,14 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
                     dma16(rk, kl + (uint32_t)ti * 1024u, voff);
             }
         }
-    }
+    };
+    // The first RING tiles with Q.  The compiler's own wait for Q (it does
+    // not see the tile loads, so it waits for all loads) is taken here.
+#pragma unroll
+    for (int t = 0; t < RING; ++t) issue_tile(t);
     wait_tile_loads<0>();
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) asm volatile("" ::"v"(qreg[kk]));
     barrier();
 
     // ---- this wave's query rows over the visible key tiles
@@ -160,9 +176,25 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        if (j >= n_w) break;
-        const uint16_t *kt = sK[j];
-        const uint16_t *vt = sV[j];
+        if (j >= n) break;
+        if constexpr (NT > RING) {
+            if (j > 0) {
+                // Tile j + RING - 1 goes to the slot of tile j - 1, which
+                // every wave is past after this barrier.  Before it, the
+                // loads issued after tile j's are at most those of tile
+                // j + RING - 2 (if it exists): RING - 2 tiles.
+                static_assert(RING == 2 || RING == 3, "ring depth");
+                if (RING == 3 && j + 1 < n)
+                    wait_tile_loads<SHARE>();
+                else
+                    wait_tile_loads<0>();
+                barrier();
+                if (j + RING - 1 < NT) issue_tile(j + RING - 1);
+            }
+        }
+        if (j >= n_w) continue;
+        const uint16_t *kt = sK[j % RING];
+        const uint16_t *vt = sV[j % RING];
         // S^T = K_j Q^T
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -209,24 +241,41 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
                 oacc[cb] = mfma32<BF16>(frag_v<D>(vt, cb, kc, lane, g), pf[kc >> 1][kc & 1], oacc[cb]);
     }
 
-    // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l)
+    // ---- epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l).  O is staged
+    // in LDS (the K tiles' space, free once every wave is past its last
+    // tile), so that each store instruction writes whole 16-byte chunks of
+    // consecutive rows.  From the accumulator layout each lane would write
+    // 8-byte pieces, spread over 32 rows per instruction: with loads and
+    // arithmetic taken out, those stores alone took 3.9 us at 600 x 256
+    // rows of d = 32, the staged ones 2.7 us.
     const Halves lh = both_halves(l_run);
     const float l_tot = lh.lo + lh.hi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_q < M) {
-        uint16_t *orow = p.O + q_base + (size_t)my_q * D;
+    static_assert(RING * TILE >= kSBM * D, "the output tile fits in the K tiles' space");
+    barrier();
+    // This wave's 32 rows, row-major with the tiles' XOR swizzle of 16-byte
+    // chunks (the 32 rows a write instruction touches spread over the banks).
+    uint16_t *so = &sK[0][0] + wave * kQRows * D;
+    const int wsw = swz<D>(l32);
 #pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
+    for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                u32x2 w = {pack2<BF16>(oacc[cb][4 * a] * inv, oacc[cb][4 * a + 1] * inv),
-                           pack2<BF16>(oacc[cb][4 * a + 2] * inv, oacc[cb][4 * a + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + cb * 32 + a * 8 + g * 4) = w;
-            }
-        if (p.LSE != nullptr && g == 0)
-            p.LSE[(size_t)sl * M + my_q] =
-                l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+        for (int a = 0; a < 4; ++a) {
+            u32x2 w = {pack2<BF16>(oacc[cb][4 * a] * inv, oacc[cb][4 * a + 1] * inv),
+                       pack2<BF16>(oacc[cb][4 * a + 2] * inv, oacc[cb][4 * a + 3] * inv)};
+            *reinterpret_cast<u32x2 *>(so + l32 * D + (((cb * 4 + a) ^ wsw) * 8) + g * 4) = w;
+        }
+    // each wave reads back only what it wrote: LDS keeps a wave's order
+    uint16_t *ob = p.O + q_base + (size_t)qw0 * D;
+#pragma unroll
+    for (int k = 0; k < kQRows * CPR / 64; ++k) {
+        const int L = lane + 64 * k;
+        const int row = L / CPR, ch = L % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(so + row * D + ((ch ^ swz<D>(row)) * 8));
+        if (qw0 + row < M) *reinterpret_cast<u32x4 *>(ob + L * 8) = v;
     }
+    if (my_q < M && p.LSE != nullptr && g == 0)
+        p.LSE[(size_t)sl * M + my_q] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
