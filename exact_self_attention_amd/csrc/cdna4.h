@@ -201,6 +201,83 @@ __device__ __forceinline__ float exps64(const f32x16 (&s)[2], float c, float neg
     return pr[0];
 }
 
+// Row max of a 32-key block (S^T layout: one query column per lane pair).
+__device__ __forceinline__ float row_max32(const f32x16 &s) {
+    float t[6];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[i] = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
+    t[5] = s[15];
+    const float mx = max3(max3(t[0], t[1], t[2]), t[3], max3(t[4], t[5], t[5]));
+    const Halves mh = both_halves(mx);
+    return fmaxf(mh.lo, mh.hi);
+}
+// P = exp2(c s + neg_m) for a 32-key block, packed into pf[ch] (16-key
+// chunks, the B operand of the P.V product); returns the lane's fp32 sum.
+template <bool BF16>
+__device__ __forceinline__ float exps32(const f32x16 &s, float c, float neg_m, u32x4 (&pf)[2]) {
+    float pr[16];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = ch * 8 + 2 * w;
+            pr[i] = fast_exp2(__builtin_fmaf(s[i], c, neg_m));
+            pr[i + 1] = fast_exp2(__builtin_fmaf(s[i + 1], c, neg_m));
+            pf[ch][w] = pack2<BF16>(pr[i], pr[i + 1]);
+        }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
+    return pr[0];
+}
+
+typedef __fp16 f16x2s __attribute__((ext_vector_type(2)));
+// P = exp2(c s + neg_m) for NB 32-key blocks, packed into pf; returns the
+// lane's sum.  With fp16 probabilities the sum is taken over the packed
+// values, two per v_dot2_f32_f16 against (1, 1) in fp32 (16 + 3 instead of
+// 31 additions per 64 keys): it is then the sum of exactly the rounded
+// values the P.V product weights V with, within 2^-11 relative of the sum
+// of the unrounded ones.  With bf16 (2^-8) the fp32 values are summed.
+template <bool BF16, int NB>
+__device__ __forceinline__ float exps_blocks(const f32x16 (&s)[NB], float c, float neg_m,
+                                             u32x4 (&pf)[NB][2]) {
+    float pr[16 * NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int i = kb * 16 + ch * 8 + 2 * w;
+                pr[i] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w], c, neg_m));
+                pr[i + 1] = fast_exp2(__builtin_fmaf(s[kb][ch * 8 + 2 * w + 1], c, neg_m));
+                pf[kb][ch][w] = pack2<BF16>(pr[i], pr[i + 1]);
+            }
+    if constexpr (BF16) {
+#pragma unroll
+        for (int w = 8 * NB; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
+        return pr[0];
+    } else {
+        const f16x2s one = {(__fp16)1.0f, (__fp16)1.0f};
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // (a vector element as the operand of __builtin_bit_cast
+                    // compiles to element 0: copy it out first)
+                    const uint32_t word = pf[kb][ch][w];
+                    acc[w] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2s, word), one, acc[w], false);
+                }
+        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+}
+
 // Causal positions of a slice's query rows.  The rows of the query heads
 // that share a key/value head follow each other, nq rows per head, so row r
 // is query r mod nq of its head and sees keys j <= r mod nq + off.

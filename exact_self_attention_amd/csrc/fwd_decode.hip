@@ -36,37 +36,6 @@ constexpr int kDWaves = 4;            // waves per workgroup, one per SIMD
 constexpr int kDBN = 32;              // keys per tile
 constexpr int kDMaxRows = kQRows;     // query rows per slice (one wave's worth)
 
-// Row max over the 16 scores a lane holds of a 32-key block, both halves.
-__device__ __forceinline__ float row_max32(const f32x16 &s) {
-    float t[6];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) t[i] = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
-    t[5] = s[15];
-    const float mx = max3(max3(t[0], t[1], t[2]), t[3], max3(t[4], t[5], t[5]));
-    const Halves mh = both_halves(mx);
-    return fmaxf(mh.lo, mh.hi);
-}
-// P = exp2(c s + neg_m) for a 32-key block, packed into pf[ch] (16-key
-// chunks, the B operand of the P.V product); returns the lane's fp32 sum.
-template <bool BF16>
-__device__ __forceinline__ float exps32(const f32x16 &s, float c, float neg_m, u32x4 (&pf)[2]) {
-    float pr[16];
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int i = ch * 8 + 2 * w;
-            pr[i] = fast_exp2(__builtin_fmaf(s[i], c, neg_m));
-            pr[i + 1] = fast_exp2(__builtin_fmaf(s[i + 1], c, neg_m));
-            pf[ch][w] = pack2<BF16>(pr[i], pr[i + 1]);
-        }
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
-    return pr[0];
-}
-
 template <int D, bool BF16, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void decode_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row

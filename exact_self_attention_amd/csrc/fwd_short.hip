@@ -19,6 +19,14 @@
 //      previous tile, and the tile RING - 1 ahead is loaded into it;
 //   3. O = O_acc / l goes through LDS to coalesced stores, with LSE.
 //
+// The softmax arithmetic (exponentials, row max, row sum) bounds this kernel
+// at d = 32, so it is trimmed: after the first tile the exponentials come
+// first and the row max only when they could overflow, fp16 row sums add
+// the packed probabilities two at a time (exps_blocks), a last tile whose
+// second 32 keys no row of the wave sees is computed as one 32-key block,
+// and the per-element mask compares a constant per register with one
+// per-lane limit.
+//
 // A workgroup needs 32 KB of LDS at d = 32, 48 KB at d = 64 and 64 KB at
 // d = 128, and 4, 3 or 2 workgroups are resident per compute unit.  (Five
 // of 32 KB do not fit on gfx950, although the occupancy query reports 5; at
@@ -53,6 +61,12 @@ constexpr int short_ring_of(int d) { return d == 64 ? 3 : short_max_keys_of(d) /
 // Waves per SIMD the register allocation must allow: as many workgroups as
 // LDS holds per compute unit.
 constexpr int short_waves_per_simd(int d) { return d == 32 ? 4 : (d == 64 ? 3 : 2); }
+// After the first tile the exponentials are taken against the running max
+// before any row max is known; they are redone after a max update only when
+// a lane's sum of the tile's probabilities exceeds this bound (below the
+// fp16 maximum, so no probability can overflow) or the lane has no running
+// max yet.
+constexpr float kShortExpFirstBound = 32768.0f;
 
 template <int D, bool BF16, bool CAUSAL>
 __device__ __forceinline__ void short_body(const FwdParams &p) {
@@ -173,6 +187,9 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     u32x4 pf[KB][2];
     float m_run = -INFINITY;  // running max of scale*log2(e)*score (may trail the true one)
     float l_run = 0.f;        // this lane's share of the running normaliser
+    // keys that some row of this wave sees, and that this lane's row sees
+    const int wave_lim = CAUSAL ? min(kv_end, wave_hi + 1) : kv_end;
+    const int row_lim = CAUSAL ? min(Lk, my_pos + 1) : Lk;
 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -195,6 +212,51 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
         if (j >= n_w) continue;
         const uint16_t *kt = sK[j % RING];
         const uint16_t *vt = sV[j % RING];
+        const int j0 = j * kBN;
+        if (wave_lim - j0 <= 32) {
+            // a last tile whose second half no row of the wave sees: one
+            // 32-key block
+            f32x16 s1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s1[r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) s1 = mfma32<BF16>(frag_k<D>(kt, 0, kk, l32, g), qreg[kk], s1);
+            if (j0 + 32 > wave_lim || (CAUSAL && j0 + 31 > wave_lo)) {
+                const int lim = row_lim - j0 - 4 * g;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s1[r] = (r >> 2) * 8 + (r & 3) < lim ? s1[r] : -INFINITY;
+            }
+            f32x16 sb[1] = {s1};
+            u32x4 pf1[1][2];
+            float lsum = 0.f;
+            bool max_first = true;
+            if (j > 0) {
+                lsum = exps_blocks<BF16, 1>(sb, c, m_run == -INFINITY ? 0.f : -m_run, pf1);
+                max_first = __any(!(lsum <= kShortExpFirstBound) || m_run == -INFINITY);
+            }
+            if (max_first) {
+                const float m_tile = row_max32(s1) * c;
+                const bool grow = m_tile > m_run + kLazy;
+                if (__any(grow)) {
+                    const float m_new = grow ? m_tile + kHeadroom : m_run;
+                    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+                }
+                lsum = exps_blocks<BF16, 1>(sb, c, m_run == -INFINITY ? 0.f : -m_run, pf1);
+            }
+            l_run += lsum;
+#pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+                    oacc[cb] = mfma32<BF16>(frag_v<D>(vt, cb, kc, lane, g), pf1[0][kc], oacc[cb]);
+            continue;
+        }
         // S^T = K_j Q^T
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -205,34 +267,42 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 s[kb] = mfma32<BF16>(frag_k<D>(kt, kb, kk, l32, g), qreg[kk], s[kb]);
-        // mask the tiles that straddle the key-length or causal limit
-        const int j0 = j * kBN;
+        // mask the tiles that straddle the key-length or causal limit:
+        // register r of block kb holds key j0 + 32 kb + 8 (r / 4) + 4 g + r % 4
         if ((j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > wave_lo)) {
+            const int lim = row_lim - j0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool ok = key < Lk && (!CAUSAL || key <= my_pos);
-                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    s[kb][r] = kb * 32 + (r >> 2) * 8 + (r & 3) < lim ? s[kb][r] : -INFINITY;
         }
         // online softmax with a lazy running max: it moves only when the
         // tile's max exceeds it by more than kLazy, then to kHeadroom above
-        // that max; output and normaliser are rescaled by exp2(m_old - m_new)
-        const float m_tile = row_max64(s) * c;  // -inf stays -inf (c > 0)
-        const bool grow = m_tile > m_run + kLazy;
-        if (__any(grow)) {
-            const float m_new = grow ? m_tile + kHeadroom : m_run;
-            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        // that max; output and normaliser are rescaled by exp2(m_old - m_new).
+        // After the first tile, exponentials first (kShortExpFirstBound).
+        float lsum = 0.f;
+        bool max_first = true;
+        if (j > 0) {
+            lsum = exps_blocks<BF16, 2>(s, c, m_run == -INFINITY ? 0.f : -m_run, pf);
+            max_first = __any(!(lsum <= kShortExpFirstBound) || m_run == -INFINITY);
         }
-        l_run += exps64<BF16>(s, c, m_run == -INFINITY ? 0.f : -m_run, pf);
+        if (max_first) {
+            const float m_tile = row_max64(s) * c;  // -inf stays -inf (c > 0)
+            const bool grow = m_tile > m_run + kLazy;
+            if (__any(grow)) {
+                const float m_new = grow ? m_tile + kHeadroom : m_run;
+                const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+            }
+            lsum = exps_blocks<BF16, 2>(s, c, m_run == -INFINITY ? 0.f : -m_run, pf);
+        }
+        l_run += lsum;
         // O^T += V_j^T P^T
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb)

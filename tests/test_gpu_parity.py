@@ -324,6 +324,34 @@ def test_gqa_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, dtype, kl):
         assert np.all(O[:, :, :Nq - Nk] == 0) and np.all(np.isneginf(LSE[:, :, :Nq - Nk]))
 
 
+PADDED_MANY_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, dtype): many padded sequences without a causal
+    # mask, every tile count among them, on the short-sequence kernel
+    (150, 4, 2, 200, 256, 32, ai.F16),
+    (70, 2, 2, 128, 200, 64, ai.BF16),
+    (65, 1, 1, 100, 128, 128, ai.F16),
+    (1030, 1, 1, 40, 64, 32, ai.BF16),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,dtype", PADDED_MANY_CASES,
+                         ids=[f"B{c[0]}H{c[1]}kv{c[2]}q{c[3]}k{c[4]}d{c[5]}{c[6]}" for c in PADDED_MANY_CASES])
+def test_padded_many_sequences(B, H, Hkv, Nq, Nk, d, dtype):
+    seed = 47_000 + B + Nk + d
+    rng = np.random.default_rng(seed)
+    kl = rng.integers(0, Nk + 1, size=B)
+    edge = [x for x in (0, 1, 63, 64, 65, Nk - 1, Nk) if x <= Nk]  # every tile count, empty and full
+    kl[:len(edge)] = edge
+    kl = [int(x) for x in rng.permutation(kl)]
+    case = ai.random_case_general(B, H, Hkv, Nq, Nk, d, dtype, seed=seed, sigma=1.5, key_len=kl)
+    gu.log(f"padded many B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype}")
+    O, LSE = gu.run_gqa(case, False)
+    sel = ai.all_rows_selection(B, H, Nq)
+    O_ref, LSE_ref = gu.oracle_rows(case, False, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"padded many B={B} d={d}", sel)
+
+
 GQA_SPLIT_CASES = [
     # (B, H, Hkv, Nq, Nk, d, causal, dtype, key_len, n_splits)
     (3, 16, 4, 1, 2000, 128, True, ai.BF16, [2000, 1, 1234], 8),
