@@ -60,6 +60,11 @@ struct MergeParams {
     int splits;
 };
 
+// Up to this many splits, all of a row's partial LSEs and output chunks are
+// loaded before any is used: one round trip to memory instead of one per
+// split and loop.
+constexpr int kMergeRegs = 8;
+
 template <bool BF16>
 __device__ __forceinline__ void merge_body(const MergeParams &p) {
     const int chunks = p.d / 4;
@@ -67,22 +72,45 @@ __device__ __forceinline__ void merge_body(const MergeParams &p) {
     const int64_t row = t / chunks;
     const int c = (int)(t - row * chunks);
     if (row >= p.rows) return;
-    float m = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_LSE[(int64_t)s * p.rows + row]);
     uint16_t *orow = p.O + row * p.d + 4 * c;
+    float m = -INFINITY, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (p.splits <= kMergeRegs) {
+        float l[kMergeRegs];
+        f32x4 o[kMergeRegs];
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) {
+            l[s] = s < p.splits ? p.part_LSE[(int64_t)s * p.rows + row] : -INFINITY;
+            o[s] = s < p.splits ? *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c)
+                                : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) m = fmaxf(m, l[s]);
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int s = 0; s < kMergeRegs; ++s) {
+                // an empty split (LSE -inf, O_s 0) has weight 0
+                const float w = l[s] == -INFINITY ? 0.f : fast_exp2((l[s] - m) * 1.44269504088896341f);
+                wsum += w;
+                acc += w * o[s];
+            }
+        }
+    } else {
+        for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_LSE[(int64_t)s * p.rows + row]);
+        if (m != -INFINITY) {
+            for (int s = 0; s < p.splits; ++s) {
+                const float l = p.part_LSE[(int64_t)s * p.rows + row];
+                if (l == -INFINITY) continue;  // an empty split (its O_s is 0)
+                const float w = fast_exp2((l - m) * 1.44269504088896341f);
+                wsum += w;
+                acc += w * *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c);
+            }
+        }
+    }
     if (m == -INFINITY) {
         *reinterpret_cast<u32x2 *>(orow) = (u32x2){0u, 0u};
         if (p.LSE != nullptr && c == 0) p.LSE[row] = -INFINITY;
         return;
-    }
-    float wsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-        const float l = p.part_LSE[(int64_t)s * p.rows + row];
-        if (l == -INFINITY) continue;  // an empty split (its O_s is 0)
-        const float w = fast_exp2((l - m) * 1.44269504088896341f);
-        wsum += w;
-        acc += w * *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c);
     }
     const float inv = 1.f / wsum;
     *reinterpret_cast<u32x2 *>(orow) =
