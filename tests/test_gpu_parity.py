@@ -324,6 +324,43 @@ def test_gqa_matches_oracle(B, H, Hkv, Nq, Nk, d, causal, dtype, kl):
         assert np.all(O[:, :, :Nq - Nk] == 0) and np.all(np.isneginf(LSE[:, :, :Nq - Nk]))
 
 
+GROWING_SCORE_CASES = [
+    # (B, H, N, d, dtype): key tiles whose K rows are scaled up tile after
+    # tile, so that later tiles' scores exceed the running max by far more
+    # than the exponentials-first bound: the redo with a row max runs
+    # (short-sequence kernel at N <= 256, streaming kernel at d = 128 above)
+    (2, 3, 256, 32, ai.F16),
+    (2, 3, 256, 64, ai.BF16),
+    (2, 3, 128, 128, ai.F16),
+    (1, 2, 1024, 128, ai.F16),
+    (1, 2, 1024, 128, ai.BF16),
+]
+
+
+def _bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == ai.F16:
+        return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d,dtype", GROWING_SCORE_CASES,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}" for c in GROWING_SCORE_CASES])
+def test_growing_scores_take_the_max_first_path(B, H, N, d, dtype, causal):
+    seed = 48_000 + N + d + causal
+    case = ai.random_case(B, H, N, d, dtype, seed=seed, sigma=1.5)
+    k = _bits_to_f32(case["K"], dtype)
+    tile = np.arange(N) // 64
+    factor = (1.0 + 4.0 * (tile % 4)).astype(np.float32)  # x1, x5, x9, x13, x1, ...
+    case["K"] = ai.round_bits(k * factor[None, None, :, None], dtype)
+    gu.log(f"growing scores B={B} H={H} N={N} d={d} {dtype} causal={causal}")
+    O, LSE = gu.run_fused(case, causal)
+    sel = ai.all_rows_selection(B, H, N)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"growing scores N={N} d={d} causal={causal}", sel)
+
+
 PADDED_MANY_CASES = [
     # (B, H, Hkv, Nq, Nk, d, dtype): many padded sequences without a causal
     # mask, every tile count among them, on the short-sequence kernel
