@@ -89,8 +89,10 @@ __device__ __forceinline__ void merge_body(const MergeParams &p) {
         if (m != -INFINITY) {
 #pragma unroll
             for (int s = 0; s < kMergeRegs; ++s) {
-                // an empty split (LSE -inf, O_s 0) has weight 0
-                const float w = l[s] == -INFINITY ? 0.f : fast_exp2((l[s] - m) * 1.44269504088896341f);
+                // an empty split (LSE -inf) is left out: its partial output
+                // was never written, and 0 times whatever it holds may be NaN
+                if (l[s] == -INFINITY) continue;
+                const float w = fast_exp2((l[s] - m) * 1.44269504088896341f);
                 wsum += w;
                 acc += w * o[s];
             }

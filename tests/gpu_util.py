@@ -66,7 +66,8 @@ def run_naive(case: dict, causal: bool, inputs=None, max_workspace_bytes=None):
     nbytes = attn.attn_fwd_naive_workspace_bytes(B, H, N)
     if max_workspace_bytes is not None:
         nbytes = max(min(nbytes, max_workspace_bytes), attn.attn_fwd_naive_workspace_bytes(1, 1, N))
-    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    # NaN-poisoned: the baseline must read only scores it wrote
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn.attn_fwd_naive(q, k, v, o, lse, workspace=ws, scale=float(case["scale"]),
@@ -85,7 +86,9 @@ def run_split(case: dict, causal: bool, n_splits=None, inputs=None):
         code = attn.ATTN_F16 if case["dtype"] == "f16" else attn.ATTN_BF16
         n_splits = attn.attn_fwd_splitkv_default_splits(code, B, H, N, d, causal)
     nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, N, d, n_splits)
-    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    # NaN-poisoned: a split with no visible key for a row writes no partial
+    # output for it, and the merge must leave that memory out entirely
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
@@ -116,7 +119,9 @@ def run_gqa_split(case: dict, causal: bool, n_splits=None, inputs=None):
         code = attn.ATTN_F16 if case["dtype"] == "f16" else attn.ATTN_BF16
         n_splits = attn.attn_fwd_gqa_splitkv_default_splits(code, B, H, Hkv, Nq, Nk, d, causal)
     nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits)
-    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    # NaN-poisoned: a split with no visible key for a row writes no partial
+    # output for it, and the merge must leave that memory out entirely
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn.attn_fwd_gqa_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
@@ -141,7 +146,9 @@ def run_masked(case: dict, causal: bool, mask: np.ndarray, n_splits=None, inputs
     else:
         B, H, Nq, d = q.shape
         nbytes = attn.attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits)
-        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+        # NaN-poisoned: a split with no visible key for a row writes no
+        # partial output for it, and the merge must leave that memory out
+        ws = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device=q.device)
         attn.attn_fwd_masked_splitkv(q, k, v, o, lse, mask=m, workspace=ws, n_splits=n_splits,
                                      scale=float(case["scale"]), causal=causal, key_len=kl)
     torch.cuda.synchronize()
