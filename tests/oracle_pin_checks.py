@@ -572,4 +572,64 @@ def check_mask_broadcast_equals_copies(lib):
     assert np.allclose(L3, L1 + c[:, 0], rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------- arbitrary-precision brute force
+def _decimal_attention(Q, K, V, scale, causal, key_len, digits=40):
+    """The definition evaluated in decimal arithmetic at ``digits`` digits,
+    from the exact values of the fp32 inputs: per row, the visible keys'
+    scores, their max, the sum of exponentials, the weighted average of V
+    and the log-sum-exp.  Returns (O, LSE) as Python lists of Decimals
+    (LSE None for a row with no visible key)."""
+    import decimal
+    ctx = decimal.Context(prec=digits)
+    D = decimal.Decimal
+    B, H, N, d = Q.shape
+    sc = D(float(np.float32(scale)))
+    O, LSE = {}, {}
+    for b in range(B):
+        L = N if key_len is None else max(0, min(N, int(key_len[b])))
+        for h in range(H):
+            for i in range(N):
+                vis = [j for j in range(L) if not causal or j <= i]
+                if not vis:
+                    O[b, h, i] = [D(0)] * d
+                    LSE[b, h, i] = None
+                    continue
+                s = {}
+                for j in vis:
+                    acc = D(0)
+                    for c in range(d):
+                        acc = ctx.add(acc, ctx.multiply(D(float(Q[b, h, i, c])), D(float(K[b, h, j, c]))))
+                    s[j] = ctx.multiply(sc, acc)
+                m = max(s.values())
+                e = {j: ctx.exp(ctx.subtract(s[j], m)) for j in vis}
+                l = sum(e.values(), D(0))
+                O[b, h, i] = [ctx.divide(sum((ctx.multiply(e[j], D(float(V[b, h, j, c]))) for j in vis), D(0)), l)
+                              for c in range(d)]
+                LSE[b, h, i] = ctx.add(m, ctx.ln(l))
+    return O, LSE
+
+
+def check_decimal_brute_force(lib):
+    """The fp64 oracle agrees with a 40-digit decimal evaluation of the
+    definition to fp64 rounding level, on small random cases with both
+    masks: a dropped term, a wrong index or a single-precision step anywhere
+    in the oracle shows up far above 1e-12."""
+    rng = _rng(4242)
+    for causal, key_len in ((False, None), (True, None), (False, [3, 0]), (True, [5, 2])):
+        Q = _randn(rng, (2, 2, 5, 4), 1.5)
+        K = _randn(rng, (2, 2, 5, 4), 1.5)
+        V = _randn(rng, (2, 2, 5, 4))
+        scale = 0.5
+        O, LSE = _run(lib, Q, K, V, scale, causal, key_len)
+        Od, Ld = _decimal_attention(Q, K, V, scale, causal, key_len)
+        for (b, h, i), row in Od.items():
+            for c, x in enumerate(row):
+                assert abs(float(O[b, h, i, c]) - float(x)) <= 1e-12 * (1.0 + abs(float(x))), \
+                    (causal, key_len, b, h, i, c, float(O[b, h, i, c]), float(x))
+            if Ld[b, h, i] is None:
+                assert np.isneginf(LSE[b, h, i])
+            else:
+                assert abs(float(LSE[b, h, i]) - float(Ld[b, h, i])) <= 1e-12, (causal, key_len, b, h, i)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
