@@ -476,6 +476,43 @@ def check_cross_zero_query_prefix_means(lib):
                     assert abs(LSE[0, h, i] - math.log(n)) < 1e-14
 
 
+def check_sparse_selection_equals_full_rows(lib):
+    """Rows picked by a shuffled, sparse (b, h, i) selection, with repeats,
+    equal the same rows of the full result bit for bit and numpy's
+    textbook rows, for grouped heads, Nq != Nk, both structural masks and an
+    additive mask.  Selected row t is the t-th triple, not the t-th row of
+    the tensor: reading the query, the causal position or the mask row from
+    t instead of (b, h, i) fails here (every full-result pin selects the
+    rows in order, where the two coincide)."""
+    rng = _rng(35)
+    for (B, H, Hkv, Nq, Nk, d, causal, kl, mshape) in [
+            (2, 6, 2, 9, 14, 8, True, [14, 5], None),
+            (3, 4, 1, 12, 7, 16, True, [7, 0, 3], None),
+            (2, 4, 4, 10, 10, 8, False, [10, 6], (2, 4, 10, 10)),
+            (2, 6, 3, 5, 16, 8, True, None, (5, 16))]:
+        Q = _randn(rng, (B, H, Nq, d), 1.5)
+        K = _randn(rng, (B, Hkv, Nk, d), 1.5)
+        V = _randn(rng, (B, Hkv, Nk, d))
+        m = None if mshape is None else _randn(rng, mshape, 1.5)
+        key_len = None if kl is None else np.array(kl, np.int32)
+        O, LSE = _run_general(lib, Q, K, V, 0.41, causal, key_len, mask=m)
+        Oref, LSEref = textbook_numpy(Q, K, V, 0.41, causal, key_len, add_mask=m)
+        n = B * H * Nq
+        flat = rng.choice(n, size=n // 3, replace=False)
+        flat = np.concatenate([flat, flat[:3]])  # repeated rows, out of order
+        rng.shuffle(flat)
+        b, rest = np.divmod(flat, H * Nq)
+        h, i = np.divmod(rest, Nq)
+        sel = np.stack([b, h, i], axis=1).astype(np.int64)
+        Os, LSEs = oracle.attn_rows(Q, K, V, 0.41, causal, key_len, sel, mask=m, lib=lib)
+        assert np.array_equal(Os, O[b, h, i])
+        assert np.array_equal(LSEs, LSE[b, h, i])
+        assert np.allclose(Os, Oref[b, h, i], rtol=1e-12, atol=1e-12)
+        fin = np.isfinite(LSEref[b, h, i])
+        assert np.array_equal(fin, np.isfinite(LSEs))
+        assert np.allclose(LSEs[fin], LSEref[b, h, i][fin], rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------ additive mask
 def check_mask_minus_inf_is_a_structural_mask(lib):
     """An additive mask of -inf above the end-aligned diagonal equals the

@@ -54,6 +54,13 @@ MUTANTS = {
                           "for (int64_t j = 1; j < n_vis; ++j)\n                for (int64_t c = 0; c < d; ++c)\n                    o[c] +="),
     "query_row_off_by_one": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
                              "const float *q  = Q + ((b * H + h) * Nq + (i > 0 ? i - 1 : 0)) * d;"),
+    # the output index t taken for the tensor row: equal only when the
+    # selection lists every row in order
+    "query_row_from_output_index": ("const float *q  = Q + ((b * H + h) * Nq + i) * d;",
+                                    "const float *q  = Q + t * d;"),
+    "causal_position_from_output_index": ("int64_t pos = i + (Nk - Nq);",
+                                          "int64_t pos = (t % Nq) + (Nk - Nq);"),
+    "mask_row_from_output_index": ("+ h * mask_sh + i * Nk;", "+ h * mask_sh + (t % Nq) * Nk;"),
 }
 
 
