@@ -4,15 +4,21 @@
 A step is one forward call (attn_fwd, or attn_fwd_gqa for grouped-query and
 cross-attention shapes; their split-key forms when the shape has too few
 work items to fill the GPU) over one batch of seeded synthetic inputs that
-are already resident in device memory.  The K timed steps are recorded into
-one HIP graph and replayed, so no host time separates the launches.  The
-default workload is the causal decoder prefill B=1 H=32 N=4096 d=128 fp16
-(scale 1/sqrt(128)), the configuration whose throughput is reported as
-TFLOP/s and as a fraction of the dense fp16 matrix-core peak.  Prints one
-JSON line.
+are already resident in device memory.  The launches cycle through several
+copies of the inputs, enough that each launch reads them from HBM rather
+than from the last-level cache.  The K timed steps are recorded into one HIP
+graph and replayed, so no host time separates the launches; the graph is
+replayed untimed for at least --warmup-seconds first, so that the clocks
+have settled, and again after the timed replay for a median and a minimum
+per launch.  The default workload is the causal decoder prefill B=1 H=32
+N=4096 d=128 fp16 (scale 1/sqrt(128)), the configuration whose throughput
+is reported as TFLOP/s and as a fraction of the dense fp16 matrix-core peak;
+the other four configurations are measured in the same run under
+``configs``.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--no-naive] [--no-graph] [--splitkv auto|on|off] [--kv-splits S]
+                  [--no-naive] [--no-graph] [--no-rotate] [--no-configs]
+                  [--splitkv auto|on|off] [--kv-splits S]
   python bench.py --copy-probe       # a plain device copy of known size, for
                                      # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
@@ -61,6 +67,13 @@ def parse():
                     help="time K plain launches instead of one replay of a graph of K launches")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the unfused attn_fwd_naive baseline")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="time every launch on one input set (warm caches) instead of "
+                         "rotating through enough copies that each launch reads from HBM")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip measuring the other configurations in the same run")
+    ap.add_argument("--stats-seconds", type=float, default=0.25,
+                    help="GPU time of the extra timed repeats behind the median and minimum")
     ap.add_argument("--copy-probe", action="store_true")
     return ap.parse_args()
 
@@ -223,6 +236,186 @@ def cpu_baseline(w, case, target_s: float):
                       f"each over its full visible key range; {flops:.3e} flops in {secs:.1f} s"}
 
 
+# Input sets cycled through by the timed launches: enough that, between two
+# uses of a set, the other sets have moved more bytes than the 256 MB
+# last-level cache (MALL) and the L2s hold, so every launch reads its inputs
+# from HBM; at least 16 for the small shapes.
+ROTATE_EVICT_BYTES = 512 << 20
+ROTATE_MIN_SETS_SMALL = 16
+ROTATE_SMALL_SET_BYTES = 64 << 20
+
+
+def input_sets(set_bytes: int) -> int:
+    n = 1 + -(-ROTATE_EVICT_BYTES // max(set_bytes, 1))
+    if set_bytes <= ROTATE_SMALL_SET_BYTES:
+        n = max(n, ROTATE_MIN_SETS_SMALL)
+    return int(n)
+
+
+class Runner:
+    """One workload on the device: R copies of its inputs and outputs and a
+    step function that launches the chosen entry point on copy i."""
+
+    def __init__(self, attn, torch, w, case, splitkv="auto", kv_splits=0, rotate=True):
+        import attn_inputs as ai
+        self.attn, self.torch, self.w, self.case = attn, torch, w, case
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        tdt = torch.float16 if w.dtype == ai.F16 else torch.bfloat16
+
+        def to_dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+        q, k, v = to_dev(case["Q"]), to_dev(case["K"]), to_dev(case["V"])
+        self.kl = None if case["key_len"] is None else torch.from_numpy(case["key_len"]).to(dev)
+        self.scale = float(w.scale)
+        self.code = attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16
+        default_splits = attn.attn_fwd_gqa_splitkv_default_splits(
+            self.code, w.B, w.H, w.kv_heads, w.q_len, w.N, w.d, w.causal)
+        use_split = splitkv == "on" or (splitkv == "auto" and (kv_splits > 1 or default_splits > 1))
+        self.n_splits = None
+        self.ws = None
+        if use_split:
+            self.n_splits = kv_splits if kv_splits > 0 else default_splits
+            self.ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(
+                w.B, w.H, w.q_len, w.d, self.n_splits) // 4, dtype=torch.float32, device=dev)
+        self.mask = None
+        if w.mask_sigma is not None:
+            self.mask = torch.from_numpy(case["mask"]).to(dev)
+            self.entry = "attn_fwd_masked_splitkv" if use_split else "attn_fwd_masked"
+        elif w.general:
+            self.entry = "attn_fwd_gqa_splitkv" if use_split else "attn_fwd_gqa"
+        else:
+            self.entry = "attn_fwd_splitkv" if use_split else "attn_fwd"
+        set_bytes = 2 * (q.numel() + k.numel() + v.numel() + q.numel()) + 4 * q.numel() // w.d
+        self.n_sets = input_sets(set_bytes) if rotate else 1
+        self.sets = []
+        for i in range(self.n_sets):
+            qi, ki, vi = (q, k, v) if i == 0 else (q.clone(), k.clone(), v.clone())
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            self.sets.append((qi, ki, vi, o, lse))
+        self.kernel = attn.attn_fwd_gqa_kernel_name(self.code, w.d, w.H, w.kv_heads, w.q_len, w.N,
+                                                    w.causal, self.mask is not None,
+                                                    self.n_splits or 0)
+
+    def step(self, i=0):
+        """Launch on the current stream (the capture stream while a graph records)."""
+        attn, w = self.attn, self.w
+        q, k, v, o, lse = self.sets[i % self.n_sets]
+        kl, scale, ws, S = self.kl, self.scale, self.ws, self.n_splits
+        e = self.entry
+        if e == "attn_fwd_splitkv":
+            attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=S, scale=scale,
+                                  causal=w.causal, key_len=kl)
+        elif e == "attn_fwd_gqa_splitkv":
+            attn.attn_fwd_gqa_splitkv(q, k, v, o, lse, workspace=ws, n_splits=S, scale=scale,
+                                      causal=w.causal, key_len=kl)
+        elif e == "attn_fwd_gqa":
+            attn.attn_fwd_gqa(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
+        elif e == "attn_fwd_masked":
+            attn.attn_fwd_masked(q, k, v, o, lse, mask=self.mask, scale=scale, causal=w.causal,
+                                 key_len=kl)
+        elif e == "attn_fwd_masked_splitkv":
+            attn.attn_fwd_masked_splitkv(q, k, v, o, lse, mask=self.mask, workspace=ws,
+                                         n_splits=S, scale=scale, causal=w.causal, key_len=kl)
+        else:
+            attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
+
+    def timed(self, steps, warmup, warmup_seconds, stats_seconds, graph=True):
+        """W untimed steps and at least warmup_seconds of back-to-back GPU work,
+        then exactly ``steps`` launches timed (wall clock between two device
+        synchronisations, HIP events on the stream around them), then more
+        timed repeats of the same launches for the median and minimum.  With
+        ``graph`` the launches are recorded once into a HIP graph and
+        replayed, so no host time separates them."""
+        torch = self.torch
+        stream = torch.cuda.current_stream(self.dev)
+        g = None
+        if graph:
+            # capture after a first launch of each set (library state, if any,
+            # is initialised outside the capture)
+            for i in range(min(self.n_sets, steps)):
+                self.step(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    self.step(i)
+            torch.cuda.synchronize()
+
+        def run():
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(steps):
+                    self.step(i)
+
+        # warmup: one replay stays queued behind the one the host waits for,
+        # so the GPU does not idle between them
+        t_w = time.perf_counter()
+        n_warm = 0
+        prev = None
+        while n_warm < warmup or time.perf_counter() - t_w < warmup_seconds:
+            run()
+            n_warm += steps
+            e = torch.cuda.Event()
+            e.record(stream)
+            if prev is not None:
+                prev.synchronize()
+            prev = e
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_s = ev0.elapsed_time(ev1) / 1e3 / steps
+        # repeats for the median and minimum, queued back to back
+        n_rep = int(min(500, max(5, stats_seconds / max(launch_s * steps, 1e-7))))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_rep)]
+        for a, b in evs:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        reps = [a.elapsed_time(b) / 1e3 / steps for a, b in evs]
+        return {"wall_s": wall, "launch_s": launch_s, "warmup_steps_run": n_warm,
+                "median_launch_s": float(np.median(reps)), "min_launch_s": float(np.min(reps)),
+                "repeats": n_rep}
+
+
+def roofline(w, key_len, launch_s):
+    """The bound and the achieved fraction of it: HBM when the flops per
+    algorithmic byte are below the machine balance (matrix-core peak / HBM
+    bandwidth), else the matrix cores."""
+    pairs = visible_pairs(w, key_len)
+    F_alg = 4.0 * w.d * pairs
+    nbytes = algorithmic_bytes(w, key_len)
+    if F_alg / nbytes < MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = nbytes / launch_s / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}
+    achieved = F_alg / launch_s / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "algorithmic_flops": F_alg}
+
+
+def config_entry(w, r, t):
+    roof = roofline(w, r.case["key_len"], t["launch_s"])
+    achieved_med = roof["achieved"] * t["launch_s"] / t["median_launch_s"]
+    return {"kernel": r.kernel, "entry": r.entry, "bound": roof["bound"], "unit": roof["unit"],
+            "achieved": roof["achieved"], "frac": roof["frac"],
+            "frac_median": achieved_med / roof["peak"],
+            "avg_launch_us": t["launch_s"] * 1e6, "median_launch_us": t["median_launch_s"] * 1e6,
+            "min_launch_us": t["min_launch_s"] * 1e6, "input_sets": r.n_sets}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -240,143 +433,67 @@ def main():
 
     w = ai.WORKLOADS[args.workload]
     case = ai.generate(w)
-    dev = torch.device("cuda:0")
-
-    def to_dev(bits):
-        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
-        return t.view(torch.float16 if w.dtype == ai.F16 else torch.bfloat16)
-
-    q, k, v = to_dev(case["Q"]), to_dev(case["K"]), to_dev(case["V"])
-    kl = None if case["key_len"] is None else torch.from_numpy(case["key_len"]).to(dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    scale = float(w.scale)
-    code = attn.ATTN_F16 if w.dtype == ai.F16 else attn.ATTN_BF16
-    default_splits = attn.attn_fwd_gqa_splitkv_default_splits(
-        code, w.B, w.H, w.kv_heads, w.q_len, w.N, w.d, w.causal)
-    use_split = args.splitkv == "on" or (args.splitkv == "auto" and
-                                         (args.kv_splits > 1 or default_splits > 1))
-    n_splits = None
-    if use_split:
-        n_splits = args.kv_splits if args.kv_splits > 0 else default_splits
-        ws = torch.empty(attn.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.q_len, w.d,
-                                                               n_splits) // 4,
-                         dtype=torch.float32, device=dev)
-    mask = None
-    if w.mask_sigma is not None:
-        mask = torch.from_numpy(case["mask"]).to(dev)
-        entry = "attn_fwd_masked_splitkv" if use_split else "attn_fwd_masked"
-    elif w.general:
-        entry = "attn_fwd_gqa_splitkv" if use_split else "attn_fwd_gqa"
-    else:
-        entry = "attn_fwd_splitkv" if use_split else "attn_fwd"
-
-    def step():
-        # on the current stream (the capture stream while a graph records)
-        if entry == "attn_fwd_splitkv":
-            attn.attn_fwd_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits, scale=scale,
-                                  causal=w.causal, key_len=kl)
-        elif entry == "attn_fwd_gqa_splitkv":
-            attn.attn_fwd_gqa_splitkv(q, k, v, o, lse, workspace=ws, n_splits=n_splits,
-                                      scale=scale, causal=w.causal, key_len=kl)
-        elif entry == "attn_fwd_gqa":
-            attn.attn_fwd_gqa(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
-        elif entry == "attn_fwd_masked":
-            attn.attn_fwd_masked(q, k, v, o, lse, mask=mask, scale=scale, causal=w.causal,
-                                 key_len=kl)
-        elif entry == "attn_fwd_masked_splitkv":
-            attn.attn_fwd_masked_splitkv(q, k, v, o, lse, mask=mask, workspace=ws,
-                                         n_splits=n_splits, scale=scale, causal=w.causal,
-                                         key_len=kl)
-        else:
-            attn.attn_fwd(q, k, v, o, lse, scale=scale, causal=w.causal, key_len=kl)
-
-    # Untimed warmup: W steps, continued until at least --warmup-seconds of
-    # GPU work has run, so that the clocks have left their idle state (the
-    # first tens of launches after an idle period run up to 25% slower).
-    t_w = time.perf_counter()
-    n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
-        step()
-        n_warm += 1
-        if n_warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    # The K timed steps: recorded once into a HIP graph and replayed, so the
-    # launches run back to back with no host time between them (a short
-    # kernel is otherwise shorter than one Python-side launch); --no-graph
-    # times K plain launches instead.
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.steps):
-                step()
-        torch.cuda.synchronize()
-        graph.replay()  # one untimed replay
-        torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for _ in range(args.steps):
-            step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    r = Runner(attn, torch, w, case, args.splitkv, args.kv_splits, rotate=not args.no_rotate)
+    t = r.timed(args.steps, args.warmup, args.warmup_seconds, args.stats_seconds,
+                graph=not args.no_graph)
+    ms_per_step = t["wall_s"] * 1e3 / args.steps
+    launch_s = t["launch_s"]
 
     F = metric_flops(w)
-    key_len = case["key_len"]
-    pairs = visible_pairs(w, key_len)
-    F_alg = 4.0 * w.d * pairs
-    kernel = attn.attn_fwd_gqa_kernel_name(code, w.d, w.H, w.kv_heads, w.q_len, w.N, w.causal,
-                                           mask is not None, n_splits or 0)
-    nbytes = algorithmic_bytes(w, key_len)
-    # the bound: HBM when the flops per algorithmic byte are below the
-    # machine balance (matrix-core peak / HBM bandwidth), else the matrix cores
-    if F_alg / nbytes < MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
-        achieved = nbytes / launch_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
-    else:
-        achieved = F_alg / launch_s / 1e12
-        peak = MFMA_PEAK_TFLOPS[w.dtype]
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak}
-    roof["traffic"] = read_traffic(kernel, w.name)
-    roof["kernel"] = kernel
+    roof = roofline(w, case["key_len"], launch_s)
+    roof.pop("algorithmic_bytes", None)
+    roof.pop("algorithmic_flops", None)
+    roof["traffic"] = read_traffic(r.kernel, w.name)
+    roof["kernel"] = r.kernel
     roof["avg_launch_us"] = launch_s * 1e6
+    roof["median_launch_us"] = t["median_launch_s"] * 1e6
+    roof["min_launch_us"] = t["min_launch_s"] * 1e6
 
     value = F / (ms_per_step / 1e3) / 1e12
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": t["warmup_steps_run"],
         "launch": "plain" if args.no_graph else "hip_graph",
-        "entry": entry,
+        "entry": r.entry, "input_sets": r.n_sets,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "Hkv": w.kv_heads, "Nq": w.q_len,
-                   "mask": None if mask is None else f"fp32 [{w.q_len}, {w.N}] shared, N(0, {w.mask_sigma}^2)",
+                   "mask": None if r.mask is None else f"fp32 [{w.q_len}, {w.N}] shared, N(0, {w.mask_sigma}^2)",
                    "causal": w.causal, "key_padding": w.key_padding, "seed": w.seed,
-                   "kv_splits": n_splits,
+                   "kv_splits": r.n_splits,
                    "global_batch": w.B, "seq_len": w.N},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[w.dtype],
         "roofline": roof,
     }
     # the unfused baseline takes self-attention shapes without a mask only
-    if not args.no_naive and not w.general and mask is None:
-        nb = naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F)
+    if not args.no_naive and not w.general and r.mask is None:
+        stream = torch.cuda.current_stream(r.dev)
+        q, k, v = r.sets[0][:3]
+        nb = naive_baseline(attn, torch, w, q, k, v, r.kl, r.scale, stream, F)
         nb["fused_speedup"] = nb["ms_per_step"] / ms_per_step
         out["naive_baseline"] = nb
+    if not args.no_configs:
+        # every configuration of the scope, measured in this run the same way
+        # (the headline's own entry is the measurement above)
+        configs = {}
+        for name in ai.WORKLOAD_ORDER:
+            if name == w.name:
+                configs[name] = config_entry(w, r, t)
+                continue
+            wc = ai.WORKLOADS[name]
+            rc = Runner(attn, torch, wc, ai.generate(wc), rotate=not args.no_rotate)
+            # at least 20 launches per replay, and enough that a replay is
+            # >= 2 ms of work
+            t_est = rc.timed(8, 0, 0.05, 0.0, graph=False)["median_launch_s"]
+            n = int(min(2000, max(20, np.ceil(2e-3 / max(t_est, 1e-7)))))
+            tc = rc.timed(n, 0, args.warmup_seconds, args.stats_seconds, graph=not args.no_graph)
+            configs[name] = config_entry(wc, rc, tc)
+            configs[name]["steps"] = n
+            del rc
+            torch.cuda.empty_cache()
+        out["configs"] = configs
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, case, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -405,12 +405,10 @@ const char *attn_status_string(attn_status_t status) {
 attn_status_t attn_fwd_kernel_name(attn_dtype_t dtype, int64_t d, int64_t N, int causal,
                                    int has_key_len, char *buf, size_t buf_len) {
     (void)has_key_len;
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-    if (N < 0 || N > kMaxN) return ATTN_ERR_INVALID_ARG;
-    if (buf == nullptr || buf_len == 0) return ATTN_ERR_INVALID_ARG;
-    std::snprintf(buf, buf_len, "%s", attn::fwd_kernel_name(dtype == ATTN_BF16, (int)d, causal != 0, N));
-    return ATTN_OK;
+    // attn_fwd is attn_fwd_gqa with one key/value head per query head and
+    // equal lengths, so the same decision names its kernel (the head count
+    // does not enter it)
+    return attn_fwd_gqa_kernel_name(dtype, d, 1, 1, N, N, causal, 0, 0, buf, buf_len);
 }
 
 attn_status_t attn_fwd_gqa_kernel_name(attn_dtype_t dtype, int64_t d, int64_t H, int64_t Hkv,

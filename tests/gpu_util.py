@@ -167,10 +167,12 @@ def oracle_rows(case: dict, causal: bool, sel: np.ndarray, mask=None):
 
 
 def sample_rows(B: int, H: int, N: int, per_head: int, seed: int) -> np.ndarray:
-    """(b, h, i) triples: per (b, h) the first and last rows, the rows around
-    128-row tile edges, plus ``per_head`` seeded random rows."""
+    """(b, h, i) triples: per (b, h) the first and last rows, the rows on
+    both sides of the 32-row wave blocks and of the 128- and 256-row query
+    tiles near the start, plus ``per_head`` seeded random rows."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 2, N - 1]
+    fixed = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513,
+             N // 2 - 1, N // 2, N - 257, N - 256, N - 2, N - 1]
     out = []
     for b in range(B):
         for h in range(H):

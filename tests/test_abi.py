@@ -59,9 +59,24 @@ def test_kernel_names(lib):
     assert lib.attn_fwd_kernel_name(0, 32, 257, False, True) == "attn_fwd_d32_f16_full"
     assert lib.attn_fwd_kernel_name(1, 64, 256, True, False) == "attn_fwd_short_d64_bf16_causal"
     assert lib.attn_fwd_kernel_name(0, 128, 128, False, False) == "attn_fwd_short_d128_f16_full"
-    assert lib.attn_fwd_kernel_name(0, 128, 129, False, False) == "attn_fwd_d128_f16_full"
+    # one query tile per head (129..256 rows at d = 128) takes the deep-ring instance
+    assert lib.attn_fwd_kernel_name(0, 128, 129, False, False) == "attn_fwd_deep_d128_f16_full"
+    assert lib.attn_fwd_kernel_name(0, 128, 256, True, False) == "attn_fwd_deep_d128_f16_causal"
+    assert lib.attn_fwd_kernel_name(0, 128, 257, True, False) == "attn_fwd_d128_f16_causal"
     with pytest.raises(lib.AttnError):
         lib.attn_fwd_kernel_name(0, 48, 256, False, False)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_kernel_name_is_the_general_decision(lib, d):
+    """attn_fwd names the kernel attn_fwd_gqa would launch for H = Hkv and
+    Nq = Nk = N: the same short / decode / deep / streaming decision."""
+    for N in [0, 1, 2, 17, 32, 33, 48, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 512, 1000, 4096]:
+        for dtype in (0, 1):
+            for causal in (False, True):
+                for H in (1, 32):
+                    assert lib.attn_fwd_kernel_name(dtype, d, N, causal, False) == \
+                        lib.attn_fwd_gqa_kernel_name(dtype, d, H, H, N, N, causal), (d, N, dtype, causal, H)
 
 
 # Fake, never-dereferenced device addresses: each call below is rejected by
