@@ -26,7 +26,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_MISALIGNED", 4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_LAUNCH",
           6: "ATTN_ERR_DEVICE"}
 EXPORTS = ["attn_fwd", "attn_fwd_gqa", "attn_fwd_naive", "attn_fwd_naive_workspace_bytes",
-           "attn_fwd_splitkv", "attn_fwd_gqa_splitkv", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_splitkv", "attn_fwd_gqa_splitkv", "attn_fwd_gqa_splitkv_static",
+           "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_splitkv_default_splits", "attn_fwd_gqa_splitkv_default_splits",
            "attn_fwd_masked", "attn_fwd_masked_splitkv", "attn_fwd_gqa_kernel_name",
            "attn_status_string", "attn_fwd_kernel_name", "attn_version"]
@@ -52,6 +53,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_gqa.restype = i32
     lib.attn_fwd_gqa_splitkv.argtypes = general + [i64, p, ctypes.c_size_t, p]
     lib.attn_fwd_gqa_splitkv.restype = i32
+    lib.attn_fwd_gqa_splitkv_static.argtypes = general + [i64, p]
+    lib.attn_fwd_gqa_splitkv_static.restype = i32
     lib.attn_fwd_masked.argtypes = general + [p, i64, i64, p]
     lib.attn_fwd_masked.restype = i32
     lib.attn_fwd_masked_splitkv.argtypes = general + [p, i64, i64, i64, p, ctypes.c_size_t, p]
@@ -169,6 +172,21 @@ def attn_fwd_gqa_splitkv(q, k, v, o, lse=None, *, workspace: torch.Tensor, n_spl
                                   _stream(stream, q.device))
     if st != 0:
         raise AttnError("attn_fwd_gqa_splitkv", st)
+
+
+def attn_fwd_gqa_splitkv_static(q, k, v, o, lse=None, *, n_splits: int, scale: float,
+                                causal: bool = False, key_len=None, stream=None) -> None:
+    """attn_fwd_gqa_splitkv with the library's own scratch: no workspace and
+    no allocation (see include/attn.h; calls on one device must not overlap)."""
+    code = _dtype_code(q)
+    _check_general(q, k, v, o, lse, key_len)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    st = lib.attn_fwd_gqa_splitkv_static(code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                         _ptr(key_len), int(n_splits), _stream(stream, q.device))
+    if st != 0:
+        raise AttnError("attn_fwd_gqa_splitkv_static", st)
 
 
 def _mask_strides(mask, q, k):

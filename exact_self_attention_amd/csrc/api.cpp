@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "kernels.h"
@@ -304,7 +305,62 @@ attn_status_t splitkv(attn_dtype_t dtype, const void *Q, const void *K, const vo
 }
 }  // namespace
 
+// Device-resident scratch of attn_fwd_gqa_splitkv_static, for callers that
+// cannot allocate: the split partials live in this file-scope array, one
+// copy on every device the library runs on, held until the process ends.
+// In host code its name is only a stand-in for the device copy: kernels get
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_SCRATCH_BYTES];
+
+namespace {
+struct ScratchAddr {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void *ptr = nullptr;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current), or nullptr.
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    ScratchAddr &s = g_scratch[dev];
+    std::call_once(s.once, [&s] {
+        void *ptr = nullptr;
+        s.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        s.ptr = s.err == hipSuccess ? ptr : nullptr;
+    });
+    return s.ptr;
+}
+}  // namespace
+
 extern "C" {
+
+attn_status_t attn_fwd_gqa_splitkv_static(attn_dtype_t dtype, const void *Q, const void *K,
+                                          const void *V, void *O, float *LSE, int64_t B,
+                                          int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                          int64_t d, float scale, int causal,
+                                          const int32_t *key_len, int64_t n_splits,
+                                          void *stream) {
+    // the argument checks first (no HIP call for a rejected call), then the
+    // size limit, then the device and the scratch address
+    const Shape sh{B, H, Hkv, Nq, Nk, d};
+    bool empty = false;
+    attn_status_t st = check_args(dtype, Q, K, V, O, LSE, sh, scale, key_len, &empty);
+    if (st != ATTN_OK) return st;
+    if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+    if (empty) return ATTN_OK;
+    const size_t need = attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits);
+    if (need == 0) return ATTN_ERR_INVALID_ARG;
+    if (need > (size_t)ATTN_STATIC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    st = check_device();
+    if (st != ATTN_OK) return st;
+    void *const ws = scratch_on_current_device();
+    if (ws == nullptr) return ATTN_ERR_DEVICE;
+    return splitkv(dtype, Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, key_len, false,
+                   nullptr, 0, 0, n_splits, ws, (size_t)ATTN_STATIC_SCRATCH_BYTES, stream);
+}
 
 attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype, const void *Q, const void *K,
                                    const void *V, void *O, float *LSE, int64_t B, int64_t H,

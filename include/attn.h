@@ -231,6 +231,35 @@ attn_status_t attn_fwd_gqa_splitkv(attn_dtype_t dtype,
                                    void *stream);
 
 /*
+ * attn_fwd_gqa_splitkv_static -- attn_fwd_gqa_splitkv without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid it).  The split partials go to a scratch array inside the
+ * library of ATTN_STATIC_SCRATCH_BYTES (64 MiB) per device, which every
+ * device the library runs on holds until the process ends.
+ *
+ * Arguments, results and errors as attn_fwd_gqa_splitkv; the caller still
+ * owns and passes Q, K, V, O, LSE and key_len.  Returns ATTN_ERR_WORKSPACE
+ * when attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits) exceeds
+ * ATTN_STATIC_SCRATCH_BYTES (use fewer splits, or attn_fwd_gqa_splitkv with
+ * a workspace), ATTN_ERR_DEVICE when the scratch address cannot be looked
+ * up.  The first call on a device looks the address up once.  All calls on
+ * one device share the one scratch array: calls that overlap in time on
+ * one device (different streams, or host threads without ordering) race
+ * and give wrong results; calls ordered on one stream are safe.  Nothing in
+ * the scratch needs to start at zero (every partial read is written first
+ * in the same call).
+ */
+#define ATTN_STATIC_SCRATCH_BYTES (64u << 20)
+attn_status_t attn_fwd_gqa_splitkv_static(attn_dtype_t dtype,
+                                          const void *Q, const void *K, const void *V,
+                                          void *O, float *LSE,
+                                          int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                                          int64_t Nk, int64_t d, float scale, int causal,
+                                          const int32_t *key_len, int64_t n_splits,
+                                          void *stream);
+
+/*
  * attn_fwd_masked_splitkv -- attn_fwd_masked over up to n_splits key
  * ranges, merged as attn_fwd_splitkv does.  Workspace and errors as
  * attn_fwd_gqa_splitkv and attn_fwd_masked; the workspace must not overlap

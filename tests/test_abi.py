@@ -290,3 +290,17 @@ def test_gqa_kernel_names(lib):
         "attn_fwd_split_mask_d128_f16_causal"
     with pytest.raises(lib.AttnError):
         lib.attn_fwd_gqa_kernel_name(f16, 128, 32, 3, 1, 4096, True)
+
+
+def test_static_scratch_entry_checks_before_any_device_call(lib):
+    """attn_fwd_gqa_splitkv_static rejects a problem whose partials exceed its
+    scratch, and bad arguments, before any HIP call (fake pointers here)."""
+    f = lib.lib.attn_fwd_gqa_splitkv_static
+    GB = 1 << 30   # tensors of 256 MiB each, spaced so that none overlaps
+    args = lambda B=1, H=32, Hkv=32, Nq=32768, Nk=32768, d=128, S=4: (
+        0, A, A + GB, A + 2 * GB, A + 3 * GB, None, B, H, Hkv, Nq, Nk, d, 0.1, 1, None, S, None)
+    WORKSPACE, INVALID = 4, 1
+    assert f(*args()) == WORKSPACE                       # 2.2 GB of partials > 64 MiB
+    assert f(*args(S=0)) == INVALID
+    assert f(*args(Hkv=5)) == INVALID
+    assert f(*args(B=0)) == 0                            # empty: no-op
