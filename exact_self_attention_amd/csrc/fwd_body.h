@@ -75,10 +75,12 @@ constexpr int kRing = 3;
 constexpr int kAhead = kRing - 1;
 // Fragment reads run this many MFMA steps (of 4 MFMAs) ahead of their use.
 constexpr int kFragAhead = 1;
-// Tile loads are issued by all waves at the start of their softmax phases
-// when d >= this (the matrix-core phase is then the longer one), else by the
-// four waves of group A right after their matrix-core work in even phases
-// (the softmax phase is then the longer one).
+// Tile loads are issued by all eight waves when d >= this, else by the four
+// waves of group A, in both cases right after a wave's matrix-core work (with
+// an additive mask: at the start of the softmax phase, before the mask
+// loads).  Issuing a 1 KB load can hold a wave up while the vector memory
+// unit works through the loads ahead of it; right after its matrix-core
+// phase the wave would otherwise wait for its last products anyway.
 constexpr int kSpreadLoadsMinD = 128;
 // At d = 128 the exponentials of a tile are taken against the running max as
 // it stands, before any row max is known; they are redone after a move only
@@ -478,9 +480,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // and the softmax of tile j in phase 2j+1; group B runs one phase later.
     // K tile j is read in phases 2j and 2j+1, V tile j in 2j+2 and 2j+3.
     // Batch j (K tile j+AHEAD, V tile j+AHEAD-1, both first read in phase
-    // 2(j+AHEAD)) is issued in phase 2j (group A, after its matrix-core
-    // work) or, with kSpreadLoads, by group B in phase 2j and group A in
-    // phase 2j+1 (at the start of their softmax of tile j).  It is waited for
+    // 2(j+AHEAD)) is issued in phase 2j by group A after its matrix-core
+    // work and, with kSpreadLoads, in phase 2j+1 by group B after its own
+    // (with a mask: by group B in phase 2j and group A in phase 2j+1, at the
+    // start of their softmax of tile j).  It is waited for
     // at the end of phase 2(j+AHEAD)-1, when each loader's share of the
     // AHEAD-1 later batches may still be in flight.  Its slots were last
     // read in phase 2j-1.  Slot arrays are passed in statically so the
@@ -493,7 +496,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         // first phase, which only loads).  With a mask: apply tile t/2's
         // mask, issue the tile loads, then load tile t/2 + 1's mask.
         if (MASK && (t & 1) && t >= 1 && (t >> 1) < n_w) apply_mask();
-        if (kSpreadLoads && (ph & 1) != grp) issue_batch(ph >> 1, k_next, v_next);
+        constexpr bool kLoadsAfterMfma = !MASK;
+        if (kSpreadLoads && !kLoadsAfterMfma && (ph & 1) != grp) issue_batch(ph >> 1, k_next, v_next);
         if (MASK && (t & 1)) issue_mask((t >> 1) + 1);
         if (t >= 0) {
             const int jj = t >> 1;
@@ -509,6 +513,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                     mfma_phase(k_cur, v_prev, std::true_type{}, std::false_type{});
                 }
                 __builtin_amdgcn_s_setprio(0);
+                if (kSpreadLoads && kLoadsAfterMfma) issue_batch(ph >> 1, k_next, v_next);
             } else if (jj < n_w) {
                 softmax(jj);
             }
