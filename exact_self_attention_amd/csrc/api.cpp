@@ -104,6 +104,7 @@ attn::FwdParams make_params(const void *Q, const void *K, const void *V, void *O
     p.mask_sb = 0;
     p.mask_sh = 0;
     p.mask_bytes = 0;
+    p.xcd_slices = 0;
     // The kernel needs a positive exp2 scale (masked scores are -inf and must
     // map to exactly 0).  A zero scale becomes 1e-30: every score times it
     // rounds to 0 against the fp32 maximum, so all weights stay exactly 1.

@@ -316,5 +316,27 @@ __device__ __forceinline__ int heavy_first_tile(int i, int n_tiles, int nq, int 
     return n_tiles - 1 - i;
 }
 
+// Launch order of a forward whose additive mask all S slices share.  The
+// n_qt * S workgroups are dealt round-robin to the 8 XCDs, each with its own
+// L2; here XCD x works on a block of A slices and n_qt * S / (8 A) query
+// tiles, so that a query tile's mask rows are read by A slices on one XCD
+// (fetched S / A times in all, instead of up to 8 times per tile) while a
+// slice's K and V are fetched by 8 A / S XCDs.  The query tiles go to the
+// XCDs in a snake over their ranks (heaviest first under a causal mask), so
+// every XCD gets the same work, and each XCD runs its tiles heaviest first.
+// Needs S % A == 0, 8 % (S / A) == 0 and n_qt % (8 A / S) == 0.
+__device__ __forceinline__ void xcd_blocked_tile(int b, int n_qt, int S, int A, bool causal, int nq,
+                                                 int m, int rows_per_tile, int &qt, int &sl) {
+    constexpr int kXcds = 8;
+    const int x = b % kXcds, local = b / kXcds;
+    const int slice_groups = S / A;
+    const int tile_groups = kXcds / slice_groups;
+    const int sg = x % slice_groups, tg = x / slice_groups;
+    const int i = local / A;  // this XCD's i-th query tile, heaviest first
+    sl = sg * A + local % A;
+    const int rank = i * tile_groups + ((i & 1) ? tile_groups - 1 - tg : tg);
+    qt = causal ? heavy_first_tile(rank, n_qt, nq, m, rows_per_tile) : rank;
+}
+
 }  // namespace cdna4
 }  // namespace attn

@@ -177,10 +177,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int per_split = p.n_qtiles * S;
     const int sp = SPLIT ? (int)blockIdx.x / per_split : 0;
     const int wg = (int)blockIdx.x - sp * per_split;
-    const int sl = wg % S;
+    int sl = wg % S;
     int qt = wg / S;
     const int M = (int)p.M;                // query rows of the slice
-    if (CAUSAL) qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kBM);
+    if (MASK && !SPLIT && p.xcd_slices > 0)
+        xcd_blocked_tile(wg, p.n_qtiles, S, p.xcd_slices, CAUSAL, p.Nq, M, kBM, qt, sl);
+    else if (CAUSAL)
+        qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kBM);
     const int Nk = (int)p.Nk;
     const int b = sl / p.Hkv;
     const size_t q_base = (size_t)sl * (size_t)M * D;

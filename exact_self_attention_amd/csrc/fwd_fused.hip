@@ -171,9 +171,39 @@ const char *fwd_fused_kernel_name(bool bf16, int d, bool causal) {
 
 bool fwd_uses_deep(const FwdParams &p) { return p.mask == nullptr && p.M <= kBM; }
 
+// Slice-group size of the XCD-blocked launch order (xcd_blocked_tile) for a
+// masked forward, or 0 for the plain order.  Only a mask repeated over the
+// heads is reused across slices; a group of A slices then shares it when
+// the mask is also repeated over batches or the group lies in one batch.
+// Among the group sizes the order allows, take the one with the least
+// estimated traffic beyond L2: K and V fetched 8 A / S times, each batch's
+// mask (S / A) / B times per batch.
+int xcd_slice_group(const FwdParams &p, int d) {
+    if (p.mask == nullptr || p.mask_sh != 0) return 0;
+    const int S = p.slices;
+    const double kv = (double)S * (double)p.Nk * d * 4.0;
+    const double mask = (double)p.M * (double)p.Nk * 4.0;
+    int best = 0;
+    double best_cost = 0.0;
+    for (int groups = 1; groups <= 8; groups *= 2) {
+        if (S % groups != 0) continue;
+        const int A = S / groups;
+        const int per_slice_xcds = 8 / groups;
+        if (p.n_qtiles % per_slice_xcds != 0) continue;
+        if (p.mask_sb != 0 && p.Hkv % A != 0) continue;
+        const double cost = kv * per_slice_xcds + mask * groups;
+        if (best == 0 || cost < best_cost || (cost == best_cost && A < best)) {
+            best = A;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_fwd_fused(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
     if (fwd_uses_decode(p)) return launch_fwd_decode(bf16, d, causal, false, p, s);
     p.n_qtiles = (int)((p.M + kBM - 1) / kBM);
+    p.xcd_slices = xcd_slice_group(p, d);
     const int64_t blocks = (int64_t)p.n_qtiles * p.slices;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -45,6 +45,9 @@ struct FwdParams {
     const float *mask;
     int64_t mask_sb, mask_sh;
     uint32_t mask_bytes;
+    // > 0: XCD-blocked launch order of a masked forward whose mask all the
+    // slices share, with groups of this many slices (xcd_blocked_tile).
+    int xcd_slices;
 };
 
 typedef void (*FwdKernelFn)(FwdParams);

@@ -138,8 +138,9 @@ def run_masked(case: dict, causal: bool, mask: np.ndarray, n_splits=None, inputs
     import exact_self_attention_amd as attn
     q, k, v, kl = inputs if inputs is not None else dev_inputs(case)
     m = mask_dev if mask_dev is not None else torch.from_numpy(np.ascontiguousarray(mask)).to(device())
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    # NaN-poisoned, so that a query tile the launch order missed shows up
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
     if n_splits is None:
         attn.attn_fwd_masked(q, k, v, o, lse, mask=m, scale=float(case["scale"]), causal=causal,
                              key_len=kl)

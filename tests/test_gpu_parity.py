@@ -480,6 +480,14 @@ MASK_CASES = [
     (3, 4, 1, 77, 200, 32, False, ai.F16, [200, 0, 150], "per_head", 0.2),
     (1, 4, 2, 513, 130, 32, True, ai.BF16, None, "shared", 0.0),
     (2, 2, 2, 64, 64, 128, False, ai.F16, None, "per_batch", 0.5),
+    # masks repeated over the heads take the XCD-blocked launch order; these
+    # shapes make it pick each group count (1, 2, 4 and 8 slice groups, and
+    # 2 groups inside each batch of a per-batch mask)
+    (1, 2, 2, 2048, 2048, 32, True, ai.F16, None, "shared", 0.0),
+    (1, 4, 4, 1024, 1024, 128, False, ai.BF16, None, "shared", 0.0),
+    (1, 8, 8, 512, 512, 128, True, ai.F16, None, "shared", 0.1),
+    (1, 16, 16, 256, 256, 128, True, ai.BF16, None, "shared", 0.0),
+    (2, 4, 4, 1024, 1024, 64, True, ai.F16, [1024, 700], "per_batch", 0.0),
 ]
 
 
