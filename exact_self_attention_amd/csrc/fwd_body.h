@@ -611,6 +611,32 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
             if (g == 0)
                 p.part_LSE[row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
         }
+    } else if constexpr (!DEEP) {
+        // The wave's 32 output rows go through its own 32 rows of the query
+        // staging area (it is their only reader and has read them for the
+        // last time), in the swizzled layout of the K/V tiles, and leave as
+        // 16-byte stores of whole rows: one instruction writes 4 rows.
+        char *stage = reinterpret_cast<char *>(sQ) + (size_t)rb * kQRows * D * 2;
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                u32x2 w = {pack2<BF16>(oacc[cb][4 * a] * inv, oacc[cb][4 * a + 1] * inv),
+                           pack2<BF16>(oacc[cb][4 * a + 2] * inv, oacc[cb][4 * a + 3] * inv)};
+                const int chunk = (cb * 4 + a) ^ swz<D>(l32);
+                *reinterpret_cast<u32x2 *>(stage + l32 * D * 2 + chunk * 16 + g * 8) = w;
+            }
+#pragma unroll
+        for (int it = 0; it < kQRows * CPR / 64; ++it) {
+            const int c = it * 64 + lane;
+            const int row = c / CPR, ch = c % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * D * 2 + (ch ^ swz<D>(row)) * 16);
+            if (qw0 + row < M)
+                *reinterpret_cast<u32x4 *>(p.O + q_base + (size_t)(qw0 + row) * D + ch * 8) = v;
+        }
+        if (q_ok && p.LSE != nullptr && g == 0)
+            p.LSE[(size_t)sl * M + my_q] =
+                l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     } else if (q_ok) {
         uint16_t *orow = p.O + q_base + (size_t)my_q * D;
 #pragma unroll
