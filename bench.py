@@ -239,17 +239,20 @@ def cpu_baseline(w, case, target_s: float):
 # Input sets cycled through by the timed launches: enough that, between two
 # uses of a set, the other sets have moved more bytes than the 256 MB
 # last-level cache (MALL) and the L2s hold, so every launch reads its inputs
-# from HBM; at least 16 for the small shapes.
+# from HBM; at least 16 for the small shapes, and at most 4096 (for sets
+# under 128 KB, such as the 64-row single head, the other sets then move
+# less than the MALL holds and a launch may read its inputs from there).
 ROTATE_EVICT_BYTES = 512 << 20
 ROTATE_MIN_SETS_SMALL = 16
 ROTATE_SMALL_SET_BYTES = 64 << 20
+ROTATE_MAX_SETS = 4096
 
 
 def input_sets(set_bytes: int) -> int:
     n = 1 + -(-ROTATE_EVICT_BYTES // max(set_bytes, 1))
     if set_bytes <= ROTATE_SMALL_SET_BYTES:
         n = max(n, ROTATE_MIN_SETS_SMALL)
-    return int(n)
+    return int(min(n, ROTATE_MAX_SETS))
 
 
 class Runner:

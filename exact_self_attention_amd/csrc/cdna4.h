@@ -121,6 +121,25 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t vo
                  :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
+// The same load through the compiler's builtin.  The compiler then counts it
+// in the waits it inserts itself (before a use of registers loaded earlier,
+// before LDS reads of the array it writes) and tells LDS arrays apart, so
+// loads into other arrays do not hold up reads of this one.
+__device__ __forceinline__ void dma16_tracked(__amdgpu_buffer_rsrc_t rsrc, lds_void *lds,
+                                              uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, (int)voff, 0, 0, 0);
+}
+
+// Waits until at most k of this wave's vector-memory loads are in flight,
+// for k a multiple of STEP up to 3 STEP (rounded up to one).
+template <int STEP>
+__device__ __forceinline__ void wait_tile_loads_upto(int k) {
+    if (k >= 3 * STEP) wait_tile_loads<3 * STEP>();
+    else if (k >= 2 * STEP) wait_tile_loads<2 * STEP>();
+    else if (k >= STEP) wait_tile_loads<STEP>();
+    else wait_tile_loads<0>();
+}
+
 // v_max3_f32: the largest of three floats in one instruction.
 __device__ __forceinline__ float max3(float a, float b, float c) {
     float d;

@@ -14,9 +14,12 @@
 //      S^T = K_j Q^T on the matrix cores, the online softmax update of
 //      "Self-Attention Kernel & Inference Engine from Scratch" (section
 //      "Online Softmax Formulation": running max, running normaliser,
-//      rescaled output), and O^T += V_j^T P^T.  When a slice has more
-//      tiles than slots, one barrier per tile frees the slot of the
-//      previous tile, and the tile RING - 1 ahead is loaded into it;
+//      rescaled output), and O^T += V_j^T P^T.  Only Q and tile 0 are
+//      waited for before the first tile; a barrier before each later tile
+//      publishes it, so the work on the first tiles overlaps the arrival of
+//      the rest.  When a slice has more tiles than slots, that barrier also
+//      frees the slot of the previous tile, and the tile RING - 1 ahead is
+//      loaded into it;
 //   3. O = O_acc / l goes through LDS to coalesced stores, with LSE.
 //
 // The softmax arithmetic (exponentials, row max, row sum) bounds this kernel
@@ -68,6 +71,17 @@ constexpr int short_waves_per_simd(int d) { return d == 32 ? 4 : (d == 64 ? 3 : 
 // max yet.
 constexpr float kShortExpFirstBound = 32768.0f;
 
+// LDS slot I of the K (IS_V false) or V ring: one array per slot, so that the
+// compiler, which sees the tile loads, can tell a slot still being filled
+// from one being read.
+template <int D, int I, bool IS_V>
+struct ShortSlot {
+    __device__ static uint16_t *get() {
+        __shared__ __attribute__((aligned(1024))) uint16_t buf[kBN * D];
+        return buf;
+    }
+};
+
 template <int D, bool BF16, bool CAUSAL>
 __device__ __forceinline__ void short_body(const FwdParams &p) {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
@@ -84,8 +98,13 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     static_assert((2 * TILE_INSTR) % SW == 0, "tile load split");
     static_assert(KB == 2, "the softmax arithmetic assumes 64-key tiles");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[RING][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[RING][TILE];
+    static_assert(RING <= 4, "ring slots");
+    uint16_t *const sK[4] = {ShortSlot<D, 0, false>::get(), ShortSlot<D, 1, false>::get(),
+                             RING > 2 ? ShortSlot<D, 2, false>::get() : nullptr,
+                             RING > 3 ? ShortSlot<D, 3, false>::get() : nullptr};
+    uint16_t *const sV[4] = {ShortSlot<D, 0, true>::get(), ShortSlot<D, 1, true>::get(),
+                             RING > 2 ? ShortSlot<D, 2, true>::get() : nullptr,
+                             RING > 3 ? ShortSlot<D, 3, true>::get() : nullptr};
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -144,34 +163,38 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     for (int kk = 0; kk < DK; ++kk)
         qreg[kk] = my_q < M ? *reinterpret_cast<const u32x4 *>(Qp + (size_t)my_q * D + (2 * kk + g) * 8)
                             : (u32x4){0u, 0u, 0u, 0u};
+    static_assert(TILE_INSTR % SW == 0, "a load's tile (K or V) is the same in every wave");
+    // Every wave issues the same loads whatever the key length: a tile at or
+    // past the last visible one gets an empty range (its loads write zeros
+    // and read no memory), so the number of loads in flight at each point is
+    // known at compile time, to the explicit waits and to the compiler's.
     auto issue_tile = [&](int t) {
-        if (t < n) {
-            const int rows = min(kBN, Lk - t * kBN);
-            const i32x4 rk = make_rsrc(Kp + (size_t)t * kBN * D, (uint32_t)(rows * D * 2));
-            const i32x4 rv = make_rsrc(Vp + (size_t)t * kBN * D, (uint32_t)(rows * D * 2));
-            const uint32_t kl = (uint32_t)(uintptr_t)(lds_void *)sK[t % RING];
-            const uint32_t vl = (uint32_t)(uintptr_t)(lds_void *)sV[t % RING];
+        const int rows = t < n ? min(kBN, Lk - t * kBN) : 0;
+        const size_t off = t < n ? (size_t)t * kBN * D : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Kp + off), (short)0, rows * D * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Vp + off), (short)0, rows * D * 2, kBufferWord3);
 #pragma unroll
-            for (int i = 0; i < SHARE; ++i) {
-                const int u = wave_u + SW * i;
-                const bool is_v = u >= TILE_INSTR;
-                const int ti = is_v ? u - TILE_INSTR : u;
-                const int P = 64 * ti + lane;
-                const int row = P / CPR;
-                const int ch = (P % CPR) ^ swz<D>(row);
-                const uint32_t voff = (uint32_t)(row * D * 2 + ch * 16);
-                if (is_v)
-                    dma16(rv, vl + (uint32_t)ti * 1024u, voff);
-                else
-                    dma16(rk, kl + (uint32_t)ti * 1024u, voff);
-            }
+        for (int i = 0; i < SHARE; ++i) {
+            const int u = wave_u + SW * i;
+            const bool is_v = SW * i >= TILE_INSTR;
+            const int ti = is_v ? u - TILE_INSTR : u;
+            const int P = 64 * ti + lane;
+            const int row = P / CPR;
+            const int ch = (P % CPR) ^ swz<D>(row);
+            const uint32_t voff = (uint32_t)(row * D * 2 + ch * 16);
+            uint16_t *slot = is_v ? sV[t % RING] : sK[t % RING];
+            dma16_tracked(is_v ? rv : rk, (lds_void *)(slot + ti * 512), voff);
         }
     };
-    // The first RING tiles with Q.  The compiler's own wait for Q (it does
-    // not see the tile loads, so it waits for all loads) is taken here.
+    // Q first, then the first RING tiles.  Only tile 0 (and Q) must have
+    // arrived before the first tile's work; each later tile is waited for
+    // when its turn comes, so the work on the first tiles overlaps the
+    // arrival of the rest.
 #pragma unroll
     for (int t = 0; t < RING; ++t) issue_tile(t);
-    wait_tile_loads<0>();
+    wait_tile_loads<(RING - 1) * SHARE>();
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) asm volatile("" ::"v"(qreg[kk]));
     barrier();
@@ -194,18 +217,15 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         if (j >= n) break;
-        if constexpr (NT > RING) {
-            if (j > 0) {
-                // Tile j + RING - 1 goes to the slot of tile j - 1, which
-                // every wave is past after this barrier.  Before it, the
-                // loads issued after tile j's are at most those of tile
-                // j + RING - 2 (if it exists): RING - 2 tiles.
-                static_assert(RING == 2 || RING == 3, "ring depth");
-                if (RING == 3 && j + 1 < n)
-                    wait_tile_loads<SHARE>();
-                else
-                    wait_tile_loads<0>();
-                barrier();
+        if (j > 0) {
+            // Tile j is in once the loads issued after its own are all that
+            // may still be in flight: those of tiles j + 1 .. j + RING - 2
+            // (below NT).  With fewer slots than tiles, tile j + RING - 1
+            // then goes to the slot of tile j - 1, which every wave is past
+            // after this barrier.
+            wait_tile_loads_upto<SHARE>((min(j + RING - 2, NT - 1) - j) * SHARE);
+            barrier();
+            if constexpr (NT > RING) {
                 if (j + RING - 1 < NT) issue_tile(j + RING - 1);
             }
         }
@@ -321,11 +341,14 @@ __device__ __forceinline__ void short_body(const FwdParams &p) {
     const Halves lh = both_halves(l_run);
     const float l_tot = lh.lo + lh.hi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    static_assert(RING * TILE >= kSBM * D, "the output tile fits in the K tiles' space");
+    static_assert(2 * TILE >= kSBM * D, "the output tile fits in the first two K slots");
+    // loads of tiles the loop did not reach (empty ranges, zeros) may still
+    // be writing their slots
+    wait_tile_loads<0>();
     barrier();
     // This wave's 32 rows, row-major with the tiles' XOR swizzle of 16-byte
     // chunks (the 32 rows a write instruction touches spread over the banks).
-    uint16_t *so = &sK[0][0] + wave * kQRows * D;
+    uint16_t *so = sK[wave >> 1] + (wave & 1) * kQRows * D;
     const int wsw = swz<D>(l32);
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
