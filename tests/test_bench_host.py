@@ -86,3 +86,17 @@ def test_read_traffic_needs_the_current_source_digest(tmp_path, monkeypatch):
 def test_kernel_sources_exist():
     for path in bench.KERNEL_SOURCES:
         assert os.path.exists(path), path
+
+
+def test_input_sets_evict_the_caches_within_bounds():
+    # enough copies that the others move more than the eviction target
+    # between two uses of one copy; at least 16 for small sets, at most 4096
+    big = 200 << 20
+    n = bench.input_sets(big)
+    assert (n - 1) * big >= bench.ROTATE_EVICT_BYTES and n >= 2
+    assert bench.input_sets(32 << 20) == max(bench.ROTATE_MIN_SETS_SMALL,
+                                            1 + bench.ROTATE_EVICT_BYTES // (32 << 20))
+    assert bench.input_sets(1 << 20) == 513          # 512 MiB of other copies
+    assert bench.input_sets(16 << 10) == bench.ROTATE_MAX_SETS
+    assert bench.input_sets(1) == bench.ROTATE_MAX_SETS
+    assert bench.input_sets(4 << 30) == 2
