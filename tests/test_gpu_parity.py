@@ -415,6 +415,14 @@ GQA_SPLIT_CASES = [
     (2, 8, 8, 1, 600, 64, False, ai.F16, [600, 0], 64),
     (2, 8, 2, 8, 1500, 64, True, ai.BF16, [1500, 333], 5),
     (1, 4, 1, 7, 300, 32, True, ai.F16, None, 2),
+    # decode shapes (at most 32 rows per key/value head): many heads of
+    # unequal key length with empty ones between them, more splits than
+    # tiles, and no visible key at all
+    (9, 8, 2, 1, 700, 128, False, ai.F16, [0, 1, 33, 700, 0, 64, 65, 5, 0], 1),
+    (9, 8, 2, 4, 700, 64, True, ai.BF16, [0, 1, 33, 700, 0, 64, 65, 5, 0], 3),
+    (4, 4, 4, 1, 3000, 32, False, ai.BF16, [3000, 17, 2900, 1], 7),
+    (5, 8, 4, 1, 2500, 128, True, ai.BF16, [2500, 1200, 2100, 37, 2499], 4),
+    (3, 4, 2, 2, 100, 64, True, ai.F16, [0, 0, 0], 2),
 ]
 
 
