@@ -406,6 +406,42 @@ def test_padded_many_sequences(B, H, Hkv, Nq, Nk, d, dtype):
     gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"padded many B={B} d={d}", sel)
 
 
+# The longest sequences, far past the workloads' 32768: positions, tile
+# counts and offsets in the hundreds of thousands (and a million keys for
+# the split decode), on sampled rows that include the tile boundaries, the
+# last rows and a key length that ends inside a tile.
+LONG_CASES = [
+    # (B, H, N, d, causal, dtype, key_len)
+    (1, 2, 262144, 64, True, ai.F16, [262144 - 1000]),
+    (1, 1, 131072, 128, False, ai.BF16, [131072 - 33]),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dtype,kl", LONG_CASES,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{'c' if c[4] else 'f'}{c[5]}" for c in LONG_CASES])
+def test_longest_sequences(B, H, N, d, causal, dtype, kl):
+    case = ai.random_case(B, H, N, d, dtype, seed=60_000 + N + d, key_len=kl)
+    gu.log(f"longest B={B} H={H} N={N} d={d} causal={causal} {dtype}")
+    O, LSE = gu.run_fused(case, causal)
+    sel = gu.sample_rows(B, H, N, 32, seed=60_100 + N)
+    O_ref, LSE_ref = gu.oracle_rows(case, causal, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, dtype, f"longest N={N}", sel)
+
+
+def test_million_key_decode_split():
+    # one new token of 8 query heads against a history of about 2^20 keys,
+    # through the split decode with the library's split count; every row
+    B, H, Hkv, Nq, Nk, d = 1, 8, 1, 1, 1 << 20, 128
+    case = ai.random_case_general(B, H, Hkv, Nq, Nk, d, ai.BF16, seed=61_000, key_len=[Nk - 77])
+    gu.log(f"million-key decode B={B} H={H} Hkv={Hkv} Nk={Nk} d={d}")
+    O, LSE, _ = gu.run_gqa_split(case, True)
+    sel = ai.all_rows_selection(B, H, Nq)
+    O_ref, LSE_ref = gu.oracle_rows(case, True, sel)
+    Og, Lg = gu.gather(O, LSE, sel)
+    gu.assert_close(Og, Lg, O_ref, LSE_ref, ai.BF16, "million-key decode", sel)
+
+
 GQA_SPLIT_CASES = [
     # (B, H, Hkv, Nq, Nk, d, causal, dtype, key_len, n_splits)
     (3, 16, 4, 1, 2000, 128, True, ai.BF16, [2000, 1, 1234], 8),
