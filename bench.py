@@ -124,12 +124,40 @@ def algorithmic_bytes(w, key_len=None) -> int:
     return qo + kv + w.B * w.H * w.q_len * 4 + mask
 
 
+def code_only(text: str) -> str:
+    """A C/C++ source without its comments, trailing blanks and empty lines
+    (string and character literals kept), so that a change to comments
+    alone leaves the digest below as it was."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest() -> str:
-    """sha256 (first 16 hex digits) of the fused-kernel sources, in order."""
+    """sha256 (first 16 hex digits) of the fused-kernel sources' code (no
+    comments), file after file."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

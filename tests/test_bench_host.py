@@ -83,6 +83,34 @@ def test_read_traffic_needs_the_current_source_digest(tmp_path, monkeypatch):
     assert bench.read_traffic("k_a", "w_a") is None
 
 
+def test_code_only_drops_comments_and_keeps_code():
+    src = ('#include "a.h"  // the header\n'
+           '/* a block\n   over lines */\n'
+           'int x = 1;   \n'
+           '\n'
+           'const char *s = "// kept /* too */";  // gone\n'
+           "char c = '/'; int y = 2 / 3; /* inline */ int z;\n")
+    assert bench.code_only(src) == ('#include "a.h"\n'
+                                    'int x = 1;\n'
+                                    'const char *s = "// kept /* too */";\n'
+                                    "char c = '/'; int y = 2 / 3;  int z;")
+    # a comment alone does not change the code, an edit of the code does
+    assert bench.code_only(src.replace("// the header", "// another")) == bench.code_only(src)
+    assert bench.code_only(src.replace("x = 1", "x = 2")) != bench.code_only(src)
+
+
+def test_source_digest_ignores_comments(tmp_path, monkeypatch):
+    a, b = tmp_path / "a.hip", tmp_path / "b.hip"
+    a.write_text("int f() { return 1; }  // one\n")
+    b.write_text("/* two */ int g;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(a), str(b)])
+    d0 = bench.source_digest()
+    a.write_text("// a note\nint f() { return 1; }\n")
+    assert bench.source_digest() == d0
+    a.write_text("int f() { return 2; }\n")
+    assert bench.source_digest() != d0
+
+
 def test_kernel_sources_exist():
     for path in bench.KERNEL_SOURCES:
         assert os.path.exists(path), path
