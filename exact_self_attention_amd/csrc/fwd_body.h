@@ -20,16 +20,17 @@
 // division by the normaliser is deferred to the end.  The gfx950 design:
 //
 //  * Two wave groups ping-pong.  Waves 0-3 and 4-7 sit on the four SIMDs in
-//    pairs.  Phases are separated by workgroup barriers; in every phase one
-//    group issues matrix-core work (P.V of the previous tile and Q.K of the
-//    current one) while the other runs the softmax of its current tile on
-//    the vector ALU, so each SIMD keeps its matrix core and its VALU busy at
-//    the same time.
+//    pairs.  In every phase one group issues matrix-core work (P.V of the
+//    previous tile and Q.K of the current one) while the other runs the
+//    softmax of its current tile on the vector ALU, so each SIMD keeps its
+//    matrix core and its VALU busy at the same time.  A workgroup barrier
+//    ends every second phase (once per key tile).
 //  * K and V tiles go from device memory straight into LDS (buffer loads
 //    with the LDS bit: no staging registers; rows past the valid key length
 //    fall outside the buffer range and read as zero, so they are never read
-//    from memory).  Both rings hold two tiles in separate LDS arrays; a tile
-//    is fetched two phases before its first use.
+//    from memory).  K and V each cycle through a ring of 3 LDS slots (5 in
+//    the deep instances), one array per slot; a tile is fetched two tiles
+//    (four phases) before its first use.
 //  * Both tiles are row-major with their 16-byte chunks XOR-swizzled by row
 //    so that the 128-bit K fragment reads and the transposing V reads
 //    (ds_read_b64_tr_b16) are free of bank conflicts.
@@ -39,7 +40,9 @@
 //    query + 32*g, register r = key 8*(r/4) + 4*g + r%4) is the B operand of
 //    the P.V MFMA as it is; the transposing reads deliver V^T in the same key
 //    order.
-//  * Q is staged in LDS once per workgroup.  exp2 with scale*log2(e) folded
+//  * Q is staged in LDS once per workgroup and moved into each wave's VGPRs
+//    (the masked d = 128 instances re-read it from LDS; the deep instances
+//    load it straight into VGPRs).  exp2 with scale*log2(e) folded
 //    into one FMA.  Lazy running max: it moves only when a tile's max
 //    exceeds it by more than 2^8, and then a little above that max, so the
 //    output and normaliser are rarely rescaled; the result is the same and
@@ -49,7 +52,13 @@
 //  * Causal and key-padding masks: the loop stops at the last key tile any
 //    row of the workgroup can see, each wave skips tiles wholly after its
 //    rows, and per-element masking runs only on tiles that straddle a
-//    boundary.  Causal grids launch the heaviest query tiles first.
+//    boundary.  Causal grids launch the heaviest query tiles first; a masked
+//    launch whose mask all slices share groups its work by XCD
+//    (xcd_blocked_tile) so that the mask rows are reused in each L2.
+//  * The output leaves through LDS (each wave's 32 rows, in the tiles'
+//    swizzled layout) as 16-byte stores of whole rows.  The deep instances,
+//    which have no query staging area, store 8-byte pieces directly; the
+//    split-key instances write fp32 partials.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
