@@ -1,7 +1,10 @@
 // gfx950 (CDNA4) device building blocks shared by the attention kernels:
 // vector types, the 32x32x16 matrix-core product, 16-bit packing, exp2, the
-// cross-half lane exchange, the LDS tile swizzle, the raw workgroup barrier,
-// buffer resources and direct-to-LDS 16-byte loads.
+// cross-half lane exchange, the LDS tile swizzle and fragment reads, the
+// softmax arithmetic on a wave's scores, the raw workgroup barrier, buffer
+// resources, direct-to-LDS 16-byte loads (inline and compiler-tracked) with
+// their counted waits, the causal row positions of a slice, and the launch
+// orders (heaviest query tiles first; XCD-blocked for a shared mask).
 #pragma once
 
 #include <hip/hip_runtime.h>
