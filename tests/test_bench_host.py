@@ -112,8 +112,13 @@ def test_source_digest_ignores_comments(tmp_path, monkeypatch):
 
 
 def test_kernel_sources_exist():
+    import re
     for path in bench.KERNEL_SOURCES:
         assert os.path.exists(path), path
+        # code_only reads ' and " as literal delimiters: digit separators
+        # and raw strings would confuse it
+        text = open(path, encoding="utf-8").read()
+        assert not re.search(r"[0-9]'[0-9]", text) and 'R"(' not in text, path
 
 
 def test_input_sets_evict_the_caches_within_bounds():
