@@ -45,6 +45,10 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_self_attention_amd", "csrc", f)
                             "fwd_fused.hip", "fwd_masked.hip", "fwd_short.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 COPY_PROBE_BYTES = 1 << 30
+# dense fp16/bf16 matrix-core flops per clock per compute unit: four SIMDs,
+# each finishing a 32x32x16 MFMA (32768 flops) every 32 clocks
+MFMA_FLOPS_PER_CLK_CU = 4096
+HIP_ATTR_CLOCK_RATE = 5   # hipDeviceAttributeClockRate (peak clock, kHz)
 
 
 def parse():
@@ -189,6 +193,60 @@ def copy_probe():
                       "copy_probe_bytes_written": COPY_PROBE_BYTES, "launches": 5}))
 
 
+def device_mfma_peak(torch):
+    """The matrix-core peak of the device in this process from its compute
+    units and peak clock (hipDeviceGetAttribute), beside the nominal figure;
+    None where the runtime cannot be asked."""
+    import ctypes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = None
+    for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+        try:
+            hip = ctypes.CDLL(name)
+        except OSError:
+            continue
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_CLOCK_RATE, 0) == 0 \
+                and 1e5 <= v.value <= 1e7:
+            khz = v.value
+            break
+    if khz is None:
+        return {"cus": cus, "clock_mhz": None, "tflops": None}
+    return {"cus": cus, "clock_mhz": khz / 1e3,
+            "tflops": cus * khz * 1e3 * MFMA_FLOPS_PER_CLK_CU / 1e12}
+
+
+def copy_roof(torch):
+    """The practical memory roof in this run: a 1 GiB device-to-device copy
+    (bytes read + written over the median of 10 timed copies)."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(10)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    secs = float(np.median([a.elapsed_time(b) / 1e3 for a, b in evs]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": 2 * COPY_PROBE_BYTES / secs / 1e9, "bytes_read": COPY_PROBE_BYTES,
+            "bytes_written": COPY_PROBE_BYTES, "kind": "torch copy_, median of 10"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def naive_baseline(attn, torch, w, q, k, v, kl, scale, stream, F):
     """Time the unfused attn_fwd_naive (scores and probabilities through HBM)
     on the same inputs; its workspace holds at most 8 GiB of heads at once."""
@@ -259,7 +317,8 @@ def cpu_baseline(w, case, target_s: float):
     oracle.attn_rows(Q, K, V, float(case["scale"]), w.causal, kl, sel, mask=case.get("mask"))
     secs = time.perf_counter() - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"{per_head} seeded random query rows per (b,h) of all {w.B * w.H} heads, "
                       f"each over its full visible key range; {flops:.3e} flops in {secs:.1f} s"}
 
@@ -437,14 +496,24 @@ def roofline(w, key_len, launch_s):
             "frac": achieved / peak, "algorithmic_flops": F_alg}
 
 
-def config_entry(w, r, t):
+def config_entry(w, r, t, device_peak=None):
     roof = roofline(w, r.case["key_len"], t["launch_s"])
     achieved_med = roof["achieved"] * t["launch_s"] / t["median_launch_s"]
-    return {"kernel": r.kernel, "entry": r.entry, "bound": roof["bound"], "unit": roof["unit"],
-            "achieved": roof["achieved"], "frac": roof["frac"],
-            "frac_median": achieved_med / roof["peak"],
-            "avg_launch_us": t["launch_s"] * 1e6, "median_launch_us": t["median_launch_s"] * 1e6,
-            "min_launch_us": t["min_launch_s"] * 1e6, "input_sets": r.n_sets}
+    out = {"kernel": r.kernel, "entry": r.entry, "bound": roof["bound"], "unit": roof["unit"],
+           "achieved": roof["achieved"], "frac": roof["frac"],
+           "frac_median": achieved_med / roof["peak"],
+           "avg_launch_us": t["launch_s"] * 1e6, "median_launch_us": t["median_launch_s"] * 1e6,
+           "min_launch_us": t["min_launch_s"] * 1e6, "input_sets": r.n_sets}
+    if roof["bound"] == "mfma" and device_peak:
+        out["frac_device_peak"] = roof["achieved"] / device_peak
+    if roof["bound"] == "hbm":
+        # beside the algorithmic bytes: the bytes with every padded key row
+        # read, and the flops of the visible pairs per second
+        F_alg = 4.0 * w.d * visible_pairs(w, r.case["key_len"])
+        out["algorithmic_bytes"] = roof["algorithmic_bytes"]
+        out["dense_bytes"] = algorithmic_bytes(w, None)
+        out["tflops_alg"] = F_alg / t["launch_s"] / 1e12
+    return out
 
 
 def main():
@@ -475,6 +544,13 @@ def main():
     roof.pop("algorithmic_bytes", None)
     roof.pop("algorithmic_flops", None)
     roof["traffic"] = read_traffic(r.kernel, w.name)
+    dev_peak = device_mfma_peak(torch)
+    if roof["bound"] == "mfma":
+        # the same against CUs x peak clock x 4096 flops/clock of this device
+        roof["peak_device"] = dev_peak["tflops"]
+        roof["frac_device_peak"] = (roof["achieved"] / dev_peak["tflops"]
+                                    if dev_peak["tflops"] else None)
+        roof["device"] = {"cus": dev_peak["cus"], "clock_mhz": dev_peak["clock_mhz"]}
     roof["kernel"] = r.kernel
     roof["avg_launch_us"] = launch_s * 1e6
     roof["median_launch_us"] = t["median_launch_s"] * 1e6
@@ -505,13 +581,15 @@ def main():
         nb = naive_baseline(attn, torch, w, q, k, v, r.kl, r.scale, stream, F)
         nb["fused_speedup"] = nb["ms_per_step"] / ms_per_step
         out["naive_baseline"] = nb
+    # the practical memory roof on this machine, for the bandwidth-bound shapes
+    out["copy_roof"] = copy_roof(torch)
     if not args.no_configs:
         # every configuration of the scope, measured in this run the same way
         # (the headline's own entry is the measurement above)
         configs = {}
         for name in ai.WORKLOAD_ORDER:
             if name == w.name:
-                configs[name] = config_entry(w, r, t)
+                configs[name] = config_entry(w, r, t, dev_peak["tflops"])
                 continue
             wc = ai.WORKLOADS[name]
             rc = Runner(attn, torch, wc, ai.generate(wc), rotate=not args.no_rotate)
@@ -520,8 +598,17 @@ def main():
             t_est = rc.timed(8, 0, 0.05, 0.0, graph=False)["median_launch_s"]
             n = int(min(2000, max(20, np.ceil(2e-3 / max(t_est, 1e-7)))))
             tc = rc.timed(n, 0, args.warmup_seconds, args.stats_seconds, graph=not args.no_graph)
-            configs[name] = config_entry(wc, rc, tc)
+            configs[name] = config_entry(wc, rc, tc, dev_peak["tflops"])
             configs[name]["steps"] = n
+            if configs[name]["bound"] == "hbm" and rc.n_sets > 1:
+                # labelled warm-cache figure: every launch on one input set
+                del rc
+                torch.cuda.empty_cache()
+                rc = Runner(attn, torch, wc, ai.generate(wc), rotate=False)
+                tw = rc.timed(n, 0, args.warmup_seconds, args.stats_seconds,
+                              graph=not args.no_graph)
+                configs[name]["warm_avg_launch_us"] = tw["launch_s"] * 1e6
+                configs[name]["warm_median_launch_us"] = tw["median_launch_s"] * 1e6
             del rc
             torch.cuda.empty_cache()
         out["configs"] = configs
