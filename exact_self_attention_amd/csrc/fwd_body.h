@@ -448,7 +448,14 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     // dependency chains); the normaliser sums the fp32 probabilities.
     static_assert(KB == 2, "the softmax arithmetic assumes 64-key tiles");
     auto row_max = [&]() -> float { return row_max64(s); };
-    auto exps = [&](float neg_m) -> float { return exps64<BF16>(s, c_sm, neg_m, pf); };
+    // (at d = 64 the vector ALU bounds the loop, and fp16 sums take the
+    // packed probabilities two at a time with v_dot2: exps_blocks)
+    auto exps = [&](float neg_m) -> float {
+        if constexpr (D == 64)
+            return exps_blocks<BF16, 2>(s, c_sm, neg_m, pf);
+        else
+            return exps64<BF16>(s, c_sm, neg_m, pf);
+    };
     auto softmax = [&](int j) {
         const int j0 = (j + j_begin) * kBN;
         const bool need_mask = (j0 + kBN > Lk) || (CAUSAL && j0 + kBN - 1 > wave_lo);

@@ -185,17 +185,23 @@ __device__ __forceinline__ void decode_body(const FwdParams &p) {
 
     // ---- merge of the four waves' partial results.  Each wave writes its
     // unnormalised output (fp32 [32 rows][D]) over its own K slots and its
-    // running max and normaliser per row into its V slots.
+    // running max and normaliser per row into its V slots.  The 16-byte
+    // chunks of a row are XOR-swizzled by the row: a row is 512 B at d = 128,
+    // a multiple of the LDS bank width, so unswizzled the 32 rows one
+    // instruction touches would all fall on the same banks.
+    auto part_at = [&](const uint16_t *slot, int col) -> float * {
+        return const_cast<float *>(reinterpret_cast<const float *>(slot)) + l32 * D +
+               (((col >> 2) ^ (l32 & (D / 4 - 1))) << 2);
+    };
     const Halves lh = both_halves(l_run);
     const float l_mine = lh.lo + lh.hi;
     barrier();  // every wave is done reading its tiles
-    float *o_part = reinterpret_cast<float *>(&sK[wave_u][0][0]);
     float *ml_part = reinterpret_cast<float *>(&sV[wave_u][0][0]);
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-            *reinterpret_cast<f32x4 *>(o_part + l32 * D + cb * 32 + a * 8 + g * 4) =
+            *reinterpret_cast<f32x4 *>(part_at(&sK[wave_u][0][0], cb * 32 + a * 8 + g * 4)) =
                 (f32x4){oacc[cb][4 * a], oacc[cb][4 * a + 1], oacc[cb][4 * a + 2], oacc[cb][4 * a + 3]};
     if (g == 0) {
         ml_part[l32] = m_run;
@@ -232,8 +238,7 @@ __device__ __forceinline__ void decode_body(const FwdParams &p) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int w = 0; w < kDWaves; ++w)
-                        acc += wgt[w] * *reinterpret_cast<const f32x4 *>(
-                                            reinterpret_cast<const float *>(&sK[w][0][0]) + l32 * D + col);
+                        acc += wgt[w] * *reinterpret_cast<const f32x4 *>(part_at(&sK[w][0][0], col));
                     *reinterpret_cast<f32x4 *>(orow + col) = acc * inv;
                 }
         }
@@ -248,8 +253,7 @@ __device__ __forceinline__ void decode_body(const FwdParams &p) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w = 0; w < kDWaves; ++w)
-                    acc += wgt[w] * *reinterpret_cast<const f32x4 *>(
-                                        reinterpret_cast<const float *>(&sK[w][0][0]) + l32 * D + col);
+                    acc += wgt[w] * *reinterpret_cast<const f32x4 *>(part_at(&sK[w][0][0], col));
                 acc *= inv;
                 *reinterpret_cast<u32x2 *>(orow + col) =
                     (u32x2){pack2<BF16>(acc[0], acc[1]), pack2<BF16>(acc[2], acc[3])};
