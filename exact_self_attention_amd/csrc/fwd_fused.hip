@@ -60,9 +60,9 @@ struct MergeParams {
     int splits;
 };
 
-// Up to this many splits, all of a row's partial LSEs and output chunks are
-// loaded before any is used: one round trip to memory instead of one per
-// split and loop.
+// Up to this many splits, all of a row's partial LSEs are loaded at once,
+// then the output chunks of the splits that saw a key of the row: two round
+// trips to memory instead of one per split and loop.
 constexpr int kMergeRegs = 8;
 
 template <bool BF16>
@@ -79,11 +79,15 @@ __device__ __forceinline__ void merge_body(const MergeParams &p) {
         float l[kMergeRegs];
         f32x4 o[kMergeRegs];
 #pragma unroll
-        for (int s = 0; s < kMergeRegs; ++s) {
+        for (int s = 0; s < kMergeRegs; ++s)
             l[s] = s < p.splits ? p.part_LSE[(int64_t)s * p.rows + row] : -INFINITY;
-            o[s] = s < p.splits ? *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c)
-                                : (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
+        // a split that saw no key of the row (LSE = -inf) wrote no output:
+        // its partial is not read (causal rows see fewer splits)
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s)
+            o[s] = l[s] != -INFINITY
+                       ? *reinterpret_cast<const f32x4 *>(p.part_O + ((int64_t)s * p.rows + row) * p.d + 4 * c)
+                       : (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kMergeRegs; ++s) m = fmaxf(m, l[s]);
         if (m != -INFINITY) {
