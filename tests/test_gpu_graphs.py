@@ -101,3 +101,64 @@ def test_graph_replays_equal_eager_launches():
                 (r["name"], rep)
             # (-inf for rows that see no key compares equal; NaN would not)
             assert torch.equal(r["lse_graph"], r["lse_eager"]), (r["name"], rep)
+
+
+def test_concurrent_host_threads_and_streams_equal_sequential():
+    # two host threads, each launching its problems repeatedly on its own
+    # stream (default priority) while the other does the same: the C entry
+    # points run concurrently (ctypes releases the GIL), and every output
+    # equals the one a single sequential launch gives
+    import threading
+    import exact_self_attention_amd as attn
+    dev = gu.device()
+    probs = _problems()
+    runs = []
+    for name, case, causal, kind, n_splits in probs:
+        if kind == "static":  # one library scratch per device: calls on two streams race
+            continue
+        q, k, v, kl = gu.dev_inputs(case)
+        ws = None
+        if kind == "split":
+            nbytes = attn.attn_fwd_splitkv_workspace_bytes(q.shape[0], q.shape[1], q.shape[2],
+                                                           q.shape[3], n_splits)
+            ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        mask = None
+        if kind == "masked":
+            rng = np.random.Generator(np.random.PCG64(70_200))
+            mask = torch.from_numpy(rng.normal(0.0, 1.0, (q.shape[2], k.shape[2])).astype(np.float32)).to(dev)
+        ref = torch.empty_like(q)
+        _launch(attn, kind, q, k, v, ref, None, kl, float(case["scale"]), causal, n_splits, ws, mask)
+        runs.append((name, kind, causal, n_splits, q, k, v, kl, ws, mask, float(case["scale"]), ref))
+    torch.cuda.synchronize()
+
+    # split the problems between the threads; each thread owns its outputs
+    # and workspaces, so nothing is shared but the inputs
+    halves = [runs[0::2], runs[1::2]]
+    outs = [[torch.empty_like(r[4]) for r in h] for h in halves]
+    wss = [[None if r[8] is None else torch.empty_like(r[8]) for r in h] for h in halves]
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    for i, r in enumerate(halves[t]):
+                        name, kind, causal, n_splits, q, k, v, kl, _, mask, scale, _ = r
+                        _launch(attn, kind, q, k, v, outs[t][i], None, kl, scale, causal, n_splits,
+                                wss[t][i], mask)
+            s.synchronize()
+        except Exception as e:  # reported on the main thread
+            errors.append(e)
+
+    gu.log("concurrent streams: two host threads")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(2):
+        for i, r in enumerate(halves[t]):
+            assert torch.equal(outs[t][i].view(torch.int16), r[11].view(torch.int16)), r[0]
