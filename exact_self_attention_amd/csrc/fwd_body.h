@@ -163,9 +163,9 @@ template <int D, bool BF16, bool CAUSAL, bool SPLIT, bool MASK, bool DEEP = fals
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     static_assert(!(DEEP && MASK), "the deep-ring instances have no mask");
     // PAIRED (d = 128 without a mask): a workgroup barrier every second key
-    // tile instead of every tile (at the end of even tiles: the first one
-    // follows key tile 0, so the prologue waits only for it), with 5-slot
-    // rings and tiles fetched three ahead (a batch then overwrites the
+    // tile instead of every tile (after key tile 0, so that the prologue
+    // waits only for it, then after odd key tiles), with 5-slot rings and
+    // tiles fetched three ahead (a batch then overwrites the
     // slots of tiles two and three back, which a barrier always separates
     // from it).  The query tile is staged in ring slots that the prologue
     // leaves free (K 3-4 and V 2-3) and is moved to VGPRs before the first
@@ -570,8 +570,18 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         // its matrix-core phase and its softmax phase back to back: the two
         // waves of a SIMD start them in opposite order, so they still
         // overlap, and the waves are not forced into step twice per tile.
-        if (PAIRED ? (ph & 3) == 1 : (ph & 1) != 0) {
-            wait_tile_loads<(PAIRED ? AHEAD - 2 : AHEAD - 1) * SHARE + (MASK ? 8 : 0)>();
+        if constexpr (PAIRED) {
+            // after key tile 0 (its batch and the next may still be in
+            // flight), then after every odd key tile (only the newest batch)
+            if (ph == 1) {
+                wait_tile_loads<(AHEAD - 1) * SHARE>();
+                barrier();
+            } else if ((ph & 3) == 3) {
+                wait_tile_loads<(AHEAD - 2) * SHARE>();
+                barrier();
+            }
+        } else if (ph & 1) {
+            wait_tile_loads<(AHEAD - 1) * SHARE + (MASK ? 8 : 0)>();
             barrier();
         }
     };
