@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -420,17 +421,36 @@ int64_t attn_fwd_gqa_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64
         decode ? attn::fwd_decode_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0)
                : attn::fwd_split_resident_workgroups(dtype == ATTN_BF16, (int)d, causal != 0);
     if (resident <= 0) return 1;
-    // work items: (key/value head, 256-row query tile), or one per key/value
-    // head for the decode kernel
-    const int64_t rows = attn::fwd_query_rows_per_item();
-    const int64_t items = decode ? B * Hkv : ((H / Hkv) * Nq + rows - 1) / rows * B * Hkv;
-    if (items >= resident) return 1;
     const int64_t tiles = (Nk + 63) / 64;
-    int64_t s = (resident + items - 1) / items;
-    const int64_t max_s = tiles / 2 > 1 ? tiles / 2 : 1;
-    if (s > max_s) s = max_s;
-    if (s > kMaxSplits) s = kMaxSplits;
-    return s < 1 ? 1 : s;
+    int64_t max_s = tiles / 2 > 1 ? tiles / 2 : 1;
+    if (max_s > kMaxSplits) max_s = kMaxSplits;
+    if (decode) {
+        // one work item per key/value head, each over all the keys
+        const int64_t items = B * Hkv;
+        if (items >= resident) return 1;
+        const int64_t s = (resident + items - 1) / items;
+        return s > max_s ? max_s : s;
+    }
+    // work items: (key/value head, 256-row query tile).  A split covers a
+    // fixed run of key tiles, and the grid holds only the splits with work
+    // (under the causal mask a query tile sees fewer keys the earlier it
+    // is).  The count is the largest whose workgroups all fit in one
+    // resident round, so that the longest run is as short as it can be.
+    const int64_t rows = attn::fwd_query_rows_per_item();
+    const int64_t n_qt = ((H / Hkv) * Nq + rows - 1) / rows;
+    if (n_qt * B * Hkv >= resident) return 1;
+    auto busy = [&](int64_t s) {
+        probe.split_tiles = (int)((tiles + s - 1) / s);
+        return attn::fwd_split_workgroups(probe, causal != 0);
+    };
+    // busy() does not decrease as s grows: take the largest s that fits
+    int64_t lo = 1, hi = max_s;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (busy(mid) <= resident) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,

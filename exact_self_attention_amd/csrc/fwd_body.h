@@ -159,6 +159,24 @@ struct QStage<0> {
 // stream K/V and are bound by device memory), Q goes from device memory
 // straight to registers instead of through LDS, and the freed LDS deepens
 // the K/V rings to 5 slots, so 4 tiles of loads are in flight instead of 2.
+// Splits of query tile qt that have work when the keys are split into runs
+// of p.split_tiles tiles: those that start before the end of the keys its
+// rows see (all Nk keys, or under the causal mask up to the highest position
+// among its rows), and at least one, so that every tile has a workgroup.
+// fwd_split_workgroups computes the same counts on the host.
+template <bool CAUSAL>
+__device__ __forceinline__ int split_busy(const FwdParams &p, int qt) {
+    int kv_end = (int)p.Nk;
+    if (CAUSAL) {
+        const int q0 = qt * kBM;
+        int lo, hi;
+        CausalRows{p.Nq, p.causal_off}.range(q0, min(q0 + kBM, (int)p.M) - 1, lo, hi);
+        kv_end = max(0, min(kv_end, hi + 1));
+    }
+    const int n_all = (kv_end + kBN - 1) / kBN;
+    return max(1, (n_all + p.split_tiles - 1) / p.split_tiles);
+}
+
 template <int D, bool BF16, bool CAUSAL, bool SPLIT, bool MASK, bool DEEP = false>
 __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     static_assert(!(DEEP && MASK), "the deep-ring instances have no mask");
@@ -204,17 +222,62 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     const int rb = 2 * simd + grp;   // this wave's 32-row block in the tile
 
     const int S = p.slices;
-    // workgroup -> (key split, query tile, slice)
-    const int per_split = p.n_qtiles * S;
-    const int sp = SPLIT ? (int)blockIdx.x / per_split : 0;
-    const int wg = (int)blockIdx.x - sp * per_split;
-    int sl = wg % S;
-    int qt = wg / S;
     const int M = (int)p.M;                // query rows of the slice
-    if (MASK && !SPLIT && p.xcd_slices > 0)
-        xcd_blocked_tile(wg, p.n_qtiles, S, p.xcd_slices, CAUSAL, p.Nq, M, kBM, qt, sl);
-    else if (CAUSAL)
-        qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kBM);
+    // workgroup -> (query tile, slice, key split)
+    int sl, qt, sp = 0;
+    int sp_busy = 1;                       // splits of this tile with work
+    if constexpr (SPLIT) {
+        // The grid lists the query tiles in launch order, each with its
+        // splits that have work (split_busy) for every slice, the splits of
+        // one slice adjacent.  Under the causal mask the counts differ, and
+        // the tile is found from their running total, 64 tiles per step.
+        const int i = (int)blockIdx.x;
+        int k_sel, pre;
+        if constexpr (!CAUSAL) {
+            sp_busy = p.kv_splits;
+            k_sel = i / (S * sp_busy);
+            pre = k_sel * sp_busy;
+        } else {
+            k_sel = -1;
+            pre = 0;
+            int base = 0;
+            for (int k0 = 0; k0 < p.n_qtiles; k0 += 64) {
+                const int k = k0 + lane;
+                const int bk = k < p.n_qtiles
+                                   ? split_busy<CAUSAL>(p, heavy_first_tile(k, p.n_qtiles, p.Nq, M, kBM))
+                                   : 0;
+                int incl = bk;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int t = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += t;
+                }
+                const unsigned long long hit = __ballot(k < p.n_qtiles && (base + incl) * S > i);
+                if (hit != 0ull) {
+                    // (one value per wave: kept in scalar registers)
+                    const int L = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+                    sp_busy = __builtin_amdgcn_readfirstlane(__shfl(bk, L, 64));
+                    pre = base + __builtin_amdgcn_readfirstlane(__shfl(incl, L, 64)) - sp_busy;
+                    k_sel = k0 + L;
+                    break;
+                }
+                base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+            }
+            if (k_sel < 0) return;  // not in the grid's list (the same for every wave)
+        }
+        const int r = i - pre * S;
+        sl = r / sp_busy;
+        sp = r - sl * sp_busy;
+        qt = CAUSAL ? heavy_first_tile(k_sel, p.n_qtiles, p.Nq, M, kBM) : k_sel;
+    } else {
+        const int wg = (int)blockIdx.x;
+        sl = wg % S;
+        qt = wg / S;
+        if (MASK && p.xcd_slices > 0)
+            xcd_blocked_tile(wg, p.n_qtiles, S, p.xcd_slices, CAUSAL, p.Nq, M, kBM, qt, sl);
+        else if (CAUSAL)
+            qt = heavy_first_tile(qt, p.n_qtiles, p.Nq, M, kBM);
+    }
     const int Nk = (int)p.Nk;
     const int b = sl / p.Hkv;
     const size_t q_base = (size_t)sl * (size_t)M * D;
@@ -253,6 +316,18 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     if (CAUSAL) n_w = max(0, min(n, (max(0, min(kv_end, wave_hi + 1)) + kBN - 1) / kBN - j_begin));
     if (qw0 >= M) n_w = 0;
     n_w = __builtin_amdgcn_readfirstlane(n_w);  // one value per wave
+    if (SPLIT && n == 0) {
+        // no row of the tile sees a key of this split: its partial rows get
+        // only LSE = -inf, which the merge reads as "no output", and so do
+        // those of the splits after the tile's last busy one, which have no
+        // workgroup (n is the same for the whole workgroup, so every wave
+        // leaves here)
+        const int r = q0 + tid;
+        if (tid < kBM && r < M)
+            for (int s2 = sp; s2 < (sp == sp_busy - 1 ? p.kv_splits : sp + 1); ++s2)
+                p.part_LSE[((size_t)s2 * S + sl) * (size_t)M + r] = -INFINITY;
+        return;
+    }
 
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -666,8 +741,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
                                oacc[cb][4 * a + 2] * inv, oacc[cb][4 * a + 3] * inv};
                     *reinterpret_cast<f32x4 *>(orow + cb * 32 + a * 8 + g * 4) = w;
                 }
-            if (g == 0)
+            if (g == 0) {
                 p.part_LSE[row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+                // the splits after the tile's last busy one have no workgroup
+                if (sp == sp_busy - 1)
+                    for (int s2 = sp + 1; s2 < p.kv_splits; ++s2)
+                        p.part_LSE[((size_t)s2 * S + sl) * (size_t)M + my_q] = -INFINITY;
+            }
         }
     } else if constexpr (!DEEP) {
         // The wave's 32 output rows go through its own 32 rows of the query

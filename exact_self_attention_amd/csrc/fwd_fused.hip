@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "fwd_body.h"
@@ -244,12 +245,34 @@ int fwd_split_resident_workgroups(bool bf16, int d, bool causal) {
     return r;
 }
 
+int64_t fwd_split_workgroups(const FwdParams &p, bool causal) {
+    if (p.split_tiles < 1 || p.M <= 0 || p.slices <= 0) return 0;
+    const int64_t n_qt = (p.M + kBM - 1) / kBM;
+    const int64_t tiles = (p.Nk + kBN - 1) / kBN;
+    int64_t busy = 0;
+    for (int64_t t = 0; t < n_qt; ++t) {
+        int64_t n_all = tiles;
+        if (causal) {
+            // the highest position among the tile's rows (split_busy)
+            const int64_t r_lo = t * kBM, r_hi = std::min<int64_t>(p.M, r_lo + kBM) - 1;
+            const int64_t hi = (r_lo / p.Nq == r_hi / p.Nq ? r_hi % p.Nq : p.Nq - 1) + p.causal_off;
+            const int64_t kv_end = std::max<int64_t>(0, std::min<int64_t>(p.Nk, hi + 1));
+            n_all = (kv_end + kBN - 1) / kBN;
+        }
+        busy += std::max<int64_t>(1, (n_all + p.split_tiles - 1) / p.split_tiles);
+    }
+    return busy * p.slices;
+}
+
 hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStream_t s) {
     p.n_qtiles = (int)((p.M + kBM - 1) / kBM);
-    const int64_t blocks = (int64_t)p.n_qtiles * p.slices * p.kv_splits;
+    if (p.kv_splits < 1 || p.split_tiles < 1) return hipErrorInvalidConfiguration;
+    // only the (query tile, slice, split) workgroups with work, plus one for
+    // a tile that sees no key (split_busy)
+    const int64_t blocks = fwd_uses_decode(p) ? (int64_t)p.n_qtiles * p.slices * p.kv_splits
+                                              : fwd_split_workgroups(p, causal);
     if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL || p.kv_splits < 1 || p.split_tiles < 1)
-        return hipErrorInvalidConfiguration;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipError_t e;
     if (fwd_uses_decode(p)) {
         e = launch_fwd_decode(bf16, d, causal, true, p, s);

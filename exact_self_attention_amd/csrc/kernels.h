@@ -65,6 +65,10 @@ hipError_t launch_fwd_split(bool bf16, int d, bool causal, FwdParams p, hipStrea
 const char *fwd_split_kernel_name(bool bf16, int d, bool causal);
 // Workgroups of the split kernel the current device holds at once (0 on error).
 int fwd_split_resident_workgroups(bool bf16, int d, bool causal);
+// Workgroups of the streaming kernel's split grid: for each query tile the
+// splits of p.split_tiles key tiles that have work, at least one, times
+// p.slices (the decode kernel has its own grid).
+int64_t fwd_split_workgroups(const FwdParams &p, bool causal);
 int fwd_query_rows_per_item();
 
 // Streaming kernel instances with the additive mask (plain or split-key);

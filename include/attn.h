@@ -282,9 +282,12 @@ size_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t
                                         int64_t n_splits);
 
 /* A split count that lets the work items of (dtype, B, H, N, d, causal)
- * occupy every compute unit of the current device: 1 when the unsplit
- * kernel already does, else enough splits to fill the resident workgroups,
- * keeping at least two key tiles per split.  Returns 1 on any error. */
+ * occupy the compute units of the current device: 1 when the unsplit kernel
+ * already fills its resident workgroups, else the largest count (at most
+ * half the key tiles) whose workgroups with work all fit in one resident
+ * round.  Under the causal mask an early query tile sees few keys, so most
+ * of its later splits have no work and are not launched.  Returns 1 on any
+ * error. */
 int64_t attn_fwd_splitkv_default_splits(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
                                         int64_t d, int causal);
 
