@@ -465,6 +465,11 @@ GQA_SPLIT_CASES = [
     (2, 8, 2, 1000, 3000, 128, True, ai.F16, [3000, 1700], None),
     (1, 4, 4, 2500, 2500, 64, True, ai.BF16, None, None),
     (1, 4, 2, 600, 4000, 32, True, ai.F16, [3900], None),
+    # more than 64 query tiles per slice (79): a workgroup's search for its
+    # tile in the split grid takes two steps of 64 tiles; in the second,
+    # query tiles span head boundaries
+    (1, 1, 1, 20000, 20000, 64, True, ai.BF16, [19000], 3),
+    (1, 4, 1, 5000, 5000, 32, True, ai.F16, None, 2),
 ]
 
 
