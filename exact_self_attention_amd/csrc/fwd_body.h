@@ -416,9 +416,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
     float m_run = -INFINITY;  // running max of scale*log2(e)*score (may trail the true one)
     float l_run = 0.f;        // this lane's share of the running normaliser
     const float c = p.scale_log2;
-    // with a mask the scores become scale*log2(e)*s + log2(e)*mask before the
-    // softmax, which then takes them with a unit scale
-    const float c_sm = MASK ? 1.f : c;
+    // with a mask the scores become scale*s + mask (one FMA each) before the
+    // softmax, which then takes them with the factor log2(e)
+    const float c_sm = MASK ? kLog2e : c;
+    const float c_mask = c * kLn2;  // the scale itself
 
     // Additive mask: this lane's query row of it.  Row r of the slice is
     // query r mod Nq of head kvh * (M / Nq) + r / Nq; the buffer spans this
@@ -456,7 +457,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams &p) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                s[kb][r] = __builtin_fmaf(s[kb][r], c, mreg[kb][r >> 2][r & 3] * kLog2e);
+                s[kb][r] = __builtin_fmaf(s[kb][r], c_mask, mreg[kb][r >> 2][r & 3]);
         // keep these before the tile loads that follow (the compiler's wait
         // for the mask must not cover them)
         asm volatile("" : "+v"(s[0]), "+v"(s[1]));
