@@ -470,6 +470,11 @@ GQA_SPLIT_CASES = [
     # query tiles span head boundaries
     (1, 1, 1, 20000, 20000, 64, True, ai.BF16, [19000], 3),
     (1, 4, 1, 5000, 5000, 32, True, ai.F16, None, 2),
+    # more query rows than keys under the end-aligned causal mask: the first
+    # query tiles see no key at all, get one workgroup each, and that one
+    # writes LSE = -inf for every split of their rows
+    (1, 2, 2, 1000, 100, 64, True, ai.F16, None, 3),
+    (2, 4, 2, 700, 300, 128, True, ai.BF16, [300, 41], 4),
 ]
 
 
